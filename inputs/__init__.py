@@ -1,0 +1,17 @@
+"""Seeded synthetic workloads for paged-KV decode.
+
+This package only draws random numbers and lays them out; it contains none of
+the attention arithmetic. Both the HIP path (through its tests and the bench)
+and the CPU oracle read the same arrays from here.
+"""
+
+from .configs import (  # noqa: F401
+    CONFIG_NAMES,
+    GqaWorkload,
+    MlaWorkload,
+    bf16_bits_from_f32,
+    make_config,
+    make_gqa,
+    make_mla,
+    lognormal_lengths,
+)

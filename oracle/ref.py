@@ -1,0 +1,165 @@
+"""fp64 CPU oracle for single-token paged attention decode.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+bench's CPU-baseline leg, never by the library. It shares no code with the HIP
+path and reads the inputs only as raw bfloat16 bit patterns.
+
+Sources (page title, then the function or step on it):
+
+* [GQA page] kernelindex.com, "flashinfer gemini-2.5-pro / triton h7ykt0":
+  the kernel ``gqa_paged_decode_h32_kv4_d128_ps1_kernel`` (its numbered steps
+  2, 4, 7, 8 and 9) and its wrapper ``run``.
+* [MLA page] FlagGems docs, coverage page of ``flash_mla_with_kvcache.py``:
+  ``_sparse_decode_kernel`` (index masking, the 576/512 latent split).
+* [QSA page] vLLM fork, ``vllm/models/qwen4_exp/amd/ops/qsa.py``:
+  ``_qsa_sparse_paged_gqa_splitk_kernel`` (normalised partials with a base-2
+  LSE) and ``_qsa_merge_splitk_kernel`` (the LSE merge).
+
+What is computed, for one query row q_h and the rows k_j, v_j it attends to:
+
+    s_j   = sm_scale * (q_h . k_j)
+    out_h = sum_j exp(s_j) v_j / sum_j exp(s_j)
+    lse_h = log2( sum_j exp(s_j) )
+
+The online softmax and split-KV of the kernels only reorder this sum. Here the
+largest score is subtracted before ``exp`` purely to keep fp64 in range. With
+no rows, out = 0 and lse = -inf ([GQA page] step 4). Every pin of this module
+lives in ``tests/test_oracle.py``.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+LN2 = math.log(2.0)
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Decode bfloat16 bit patterns: the 16 bits are the top half of a float32."""
+    u32 = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u32.view(np.float32).astype(np.float64)
+
+
+def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, sm_scale: float):
+    """Softmax attention of the query rows ``q [H, Dqk]`` over ``k [n, Dqk]``, ``v [n, Dv]``.
+
+    Returns ``out [H, Dv]`` (fp64) and the base-2 log-sum-exp ``lse [H]``.
+    Follows [GQA page] steps 8b-9: scores scaled by ``sm_scale`` in floating
+    point, normalised exponentials, base-2 LSE of the natural-exp sum; and
+    step 4 for ``n == 0``.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    h = q.shape[0]
+    if k.shape[0] == 0:
+        return np.zeros((h, v.shape[1])), np.full(h, -np.inf)
+    s = sm_scale * (q @ k.T)                      # [H, n]
+    m = s.max(axis=1, keepdims=True)              # only keeps exp() in range
+    w = np.exp(s - m)                             # [H, n]
+    z = w.sum(axis=1)                             # [H]
+    out = (w @ v) / z[:, None]
+    lse = (m[:, 0] + np.log(z)) / LN2
+    return out, lse
+
+
+def gqa_group_of(head: int, num_qo_heads: int, num_kv_heads: int) -> int:
+    """KV head read by query head ``head``: consecutive groups of Hq/Hkv heads share one.
+
+    [GQA page] step 7 (``offs_h // gqa_ratio``); [QSA page] partial kernel
+    (``first_head = kv_head * GROUP_SIZE``).
+    """
+    return head // (num_qo_heads // num_kv_heads)
+
+
+def gqa_decode_range(q_bits, k_bits, v_bits, kv_indptr, kv_indices, sm_scale: float,
+                     b: int, tok_begin: int, tok_end: int):
+    """Attention of sequence ``b`` over its tokens ``[tok_begin, tok_end)``.
+
+    Pages are looked up through the CSR list: token ``j`` of sequence ``b`` is
+    page ``kv_indices[kv_indptr[b] + j]`` ([GQA page] steps 2 and 8a). With page
+    size 1 the page holds exactly that token. Returns ``out [Hq, D]``, ``lse [Hq]``.
+    """
+    num_qo_heads, head_dim = q_bits.shape[1], q_bits.shape[2]
+    num_kv_heads = k_bits.shape[2]
+    base = int(kv_indptr[b])
+    pages = np.asarray(kv_indices[base + tok_begin: base + tok_end], dtype=np.int64)
+    q = bf16_to_f64(q_bits[b])                                   # [Hq, D]
+    out = np.zeros((num_qo_heads, v_bits.shape[3]))
+    lse = np.full(num_qo_heads, -np.inf)
+    for g in range(num_kv_heads):
+        heads = [h for h in range(num_qo_heads)
+                 if gqa_group_of(h, num_qo_heads, num_kv_heads) == g]
+        k = bf16_to_f64(k_bits[pages, 0, g, :])                  # [n, D]
+        v = bf16_to_f64(v_bits[pages, 0, g, :])
+        o_g, l_g = attend(q[heads], k, v, sm_scale)
+        out[heads] = o_g
+        lse[heads] = l_g
+    return out, lse
+
+
+def gqa_paged_decode(q_bits, k_bits, v_bits, kv_indptr, kv_indices, sm_scale: float,
+                     batches=None):
+    """Paged GQA decode of every sequence (or of the listed ``batches``).
+
+    ``q_bits [B, Hq, D]``; pools ``[P, 1, Hkv, D]``; all bfloat16 bits.
+    Returns ``out [B, Hq, D]`` and ``lse [B, Hq]`` in fp64 (rows not listed in
+    ``batches`` are left as NaN).
+    """
+    batch = q_bits.shape[0]
+    num_qo_heads = q_bits.shape[1]
+    out = np.full((batch, num_qo_heads, v_bits.shape[3]), np.nan)
+    lse = np.full((batch, num_qo_heads), np.nan)
+    for b in (range(batch) if batches is None else batches):
+        n = int(kv_indptr[b + 1]) - int(kv_indptr[b])
+        out[b], lse[b] = gqa_decode_range(q_bits, k_bits, v_bits, kv_indptr, kv_indices,
+                                          sm_scale, b, 0, n)
+    return out, lse
+
+
+def merge_lse2(parts_out: np.ndarray, parts_lse: np.ndarray):
+    """Combine normalised partial results over disjoint key sets.
+
+    ``parts_out [S, H, D]`` holds each part's normalised output and
+    ``parts_lse [S, H]`` its base-2 LSE (-inf for a part with no keys). Weights
+    are ``2^(lse_i - max lse)``; the output is the weighted mean and the merged
+    LSE is ``max + log2(sum of weights)``. All parts empty gives 0 and -inf.
+    [QSA page] ``_qsa_merge_splitk_kernel``; the merged LSE is not written
+    there, it is the same log-sum-exp identity taken one step further.
+    """
+    parts_out = np.asarray(parts_out, dtype=np.float64)
+    parts_lse = np.asarray(parts_lse, dtype=np.float64)
+    top = parts_lse.max(axis=0)                                  # [H]
+    empty = np.isneginf(top)
+    safe_top = np.where(empty, 0.0, top)
+    w = np.where(np.isneginf(parts_lse), 0.0, np.exp2(parts_lse - safe_top[None, :]))
+    den = w.sum(axis=0)
+    out = np.einsum("sh,shd->hd", w, parts_out) / np.where(empty, 1.0, den)[:, None]
+    out[empty] = 0.0
+    lse = np.where(empty, -np.inf, safe_top + np.log2(np.where(empty, 1.0, den)))
+    return out, lse
+
+
+def mla_gather_decode(q_bits, kv_bits, indices, sm_scale: float, d_v: int,
+                      batches=None):
+    """Index-gather latent-attention decode.
+
+    For row ``b`` the keys are the pool rows ``kv[t]`` for every list entry
+    ``t = indices[b, i]`` with ``0 <= t < T``; entries outside that range are
+    masked and contribute nothing ([MLA page] ``_sparse_decode_kernel``, index
+    masking). Scores use all ``Dqk`` dims; the values are the first ``d_v``
+    dims of the same row. Every entry counts, repeated ids included.
+    Returns ``out [B, Hq, d_v]`` and base-2 ``lse [B, Hq]``.
+    """
+    batch, num_qo_heads, _ = q_bits.shape
+    pool_tokens = kv_bits.shape[0]
+    out = np.full((batch, num_qo_heads, d_v), np.nan)
+    lse = np.full((batch, num_qo_heads), np.nan)
+    for b in (range(batch) if batches is None else batches):
+        ids = np.asarray(indices[b], dtype=np.int64)
+        ids = ids[(ids >= 0) & (ids < pool_tokens)]
+        rows = bf16_to_f64(kv_bits[ids])                         # [n, Dqk]
+        out[b], lse[b] = attend(bf16_to_f64(q_bits[b]), rows, rows[:, :d_v], sm_scale)
+    return out, lse

@@ -1,0 +1,386 @@
+"""Pins of the CPU oracle: facts fixed by the pages or by mathematics.
+
+Each ``pin_*`` function takes the oracle module (normally ``oracle.ref``) and
+raises ``AssertionError`` when the oracle disagrees with a closed form, an
+invariant, a library routine or a brute-force sum. They are run once against
+the real oracle (``test_oracle.py``) and once against planted mistakes
+(``test_oracle_mutants.py``) to show that each plausible slip is caught.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from inputs import bf16_bits_from_f32, make_config, make_gqa, make_mla
+from inputs.configs import EDGE_CONST_V, EDGE_CONST_V_SEQ, EDGE_LENGTHS
+
+_CACHE = {}
+
+
+def _cfg(name):
+    if name not in _CACHE:
+        _CACHE[name] = make_config(name)
+    return _CACHE[name]
+
+
+def _small_edge():
+    """The edge batch without its three longest sequences (fast on the CPU)."""
+    if "small_edge" not in _CACHE:
+        lengths = [n if n <= 4096 else 5 for n in EDGE_LENGTHS]
+        _CACHE["small_edge"] = make_gqa(3, lengths, peaky_seq=10, const_v_seq=EDGE_CONST_V_SEQ)
+    return _CACHE["small_edge"]
+
+
+def _decode(ref, w, batches=None):
+    return ref.gqa_paged_decode(w.q, w.k_pool, w.v_pool, w.kv_indptr, w.kv_indices,
+                                w.sm_scale, batches=batches)
+
+
+def _f64(bits):
+    # Independent decode for the pins: build the float32 from the bit pattern.
+    return np.frombuffer((np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).tobytes(),
+                         dtype=np.float32).astype(np.float64).reshape(np.shape(bits))
+
+
+# ---------------------------------------------------------------- encodings
+
+def pin_bf16_decode(ref):
+    bits = np.array([0x3F80, 0xBF40, 0x4049, 0x0000, 0x8000, 0x7F80, 0x3C00], dtype=np.uint16)
+    want = [1.0, -0.75, 3.140625, 0.0, -0.0, math.inf, 2.0 ** -7]
+    got = ref.bf16_to_f64(bits)
+    assert got.dtype == np.float64
+    assert list(got) == want
+
+
+# --------------------------------------------------------- GQA special cases
+
+def pin_empty_sequence(ref):
+    w = _small_edge()
+    assert w.lengths[0] == 0
+    out, lse = _decode(ref, w, batches=[0])
+    assert np.all(out[0] == 0.0) and np.all(np.isneginf(lse[0]))
+
+
+def pin_single_token(ref):
+    """n = 1: the output is that V row exactly; the LSE is the one score over ln 2."""
+    w = _small_edge()
+    b = 1
+    assert w.lengths[b] == 1
+    out, lse = _decode(ref, w, batches=[b])
+    page = int(w.kv_indices[w.kv_indptr[b]])
+    q = _f64(w.q[b])
+    for h in range(w.num_qo_heads):
+        g = h // (w.num_qo_heads // w.num_kv_heads)
+        v = _f64(w.v_pool[page, 0, g])
+        k = _f64(w.k_pool[page, 0, g])
+        assert np.array_equal(out[b, h], v)
+        s = w.sm_scale * math.fsum(float(a) * float(c) for a, c in zip(q[h], k))
+        assert abs(lse[b, h] - s / math.log(2.0)) <= 1e-12 * max(1.0, abs(s))
+
+
+def pin_uniform_v(ref):
+    """Every token carries V = 0.75, so every head outputs 0.75."""
+    w = _small_edge()
+    b = EDGE_CONST_V_SEQ
+    out, _ = _decode(ref, w, batches=[b])
+    assert np.max(np.abs(out[b] - EDGE_CONST_V)) <= 1e-15
+
+
+def pin_equal_keys(ref):
+    """All keys equal: weights 1/n, out = mean of the V rows, lse = s/ln2 + log2 n."""
+    w = make_gqa(11, [37, 5], pool_pages=50)
+    k = w.k_pool.copy()
+    for b in range(2):
+        pages = w.kv_indices[w.kv_indptr[b]:w.kv_indptr[b + 1]]
+        k[pages] = k[pages[0]]
+    w.k_pool = k
+    out, lse = _decode(ref, w)
+    for b in range(2):
+        pages = w.kv_indices[w.kv_indptr[b]:w.kv_indptr[b + 1]]
+        n = len(pages)
+        for h in range(w.num_qo_heads):
+            g = h // 8
+            mean_v = _f64(w.v_pool[pages, 0, g]).mean(axis=0)
+            assert np.max(np.abs(out[b, h] - mean_v)) <= 1e-13
+            s = w.sm_scale * float(np.dot(_f64(w.q[b, h]), _f64(k[pages[0], 0, g])))
+            assert abs(lse[b, h] - (s / math.log(2.0) + math.log2(n))) <= 1e-12
+
+
+def pin_zero_scale(ref):
+    """sm_scale = 0 makes every weight equal: out = mean(V), lse = log2 n."""
+    w = make_gqa(12, [9, 1, 40], pool_pages=60, sm_scale=0.0)
+    out, lse = _decode(ref, w)
+    for b in range(3):
+        pages = w.kv_indices[w.kv_indptr[b]:w.kv_indptr[b + 1]]
+        for g in range(4):
+            mean_v = _f64(w.v_pool[pages, 0, g]).mean(axis=0)
+            for h in range(8 * g, 8 * g + 8):
+                assert np.max(np.abs(out[b, h] - mean_v)) <= 1e-13
+        assert np.max(np.abs(lse[b] - math.log2(len(pages)))) <= 1e-12
+
+
+def pin_brute_force_tiny(ref):
+    """The tiny batch, summed term by term in Python with exact-rounded sums.
+
+    No max is subtracted here; ``math.fsum`` rounds each sum once.
+    """
+    w = _cfg("tiny")
+    out, lse = _decode(ref, w)
+    q = _f64(w.q)
+    for b in range(w.batch):
+        pages = [int(p) for p in w.kv_indices[w.kv_indptr[b]:w.kv_indptr[b + 1]]]
+        for h in range(w.num_qo_heads):
+            g = h // 8
+            s = []
+            for p in pages:
+                k = _f64(w.k_pool[p, 0, g])
+                s.append(w.sm_scale * math.fsum(float(a) * float(c) for a, c in zip(q[b, h], k)))
+            e = [math.exp(x) for x in s]
+            z = math.fsum(e)
+            assert abs(lse[b, h] - math.log2(z)) <= 1e-12 * max(1.0, abs(math.log2(z)))
+            vrows = [_f64(w.v_pool[p, 0, g]) for p in pages]
+            for d in range(0, w.head_dim, 7):
+                o = math.fsum(ei * float(vr[d]) for ei, vr in zip(e, vrows)) / z
+                assert abs(out[b, h, d] - o) <= 1e-12
+
+
+def pin_sdpa_cross_check(ref):
+    """Against torch's scaled_dot_product_attention (CPU, float64, grouped heads)."""
+    for w in (_cfg("tiny"), _small_edge()):
+        out, lse = _decode(ref, w)
+        for b in range(w.batch):
+            pages = torch.as_tensor(w.kv_indices[w.kv_indptr[b]:w.kv_indptr[b + 1]].astype(np.int64))
+            if pages.numel() == 0:
+                continue
+            q = torch.as_tensor(_f64(w.q[b]))[:, None, :]                   # [Hq, 1, D]
+            k = torch.as_tensor(_f64(w.k_pool))[pages, 0].transpose(0, 1)  # [Hkv, n, D]
+            v = torch.as_tensor(_f64(w.v_pool))[pages, 0].transpose(0, 1)
+            o = torch.nn.functional.scaled_dot_product_attention(
+                q[None], k[None].contiguous(), v[None].contiguous(), scale=w.sm_scale,
+                enable_gqa=True)[0, :, 0, :]
+            assert np.max(np.abs(out[b] - o.numpy())) <= 1e-12
+            kk = k.repeat_interleave(w.num_qo_heads // w.num_kv_heads, dim=0)
+            scores = w.sm_scale * torch.bmm(q, kk.transpose(1, 2).contiguous())[:, 0, :]
+            l2 = (torch.logsumexp(scores, dim=-1) / math.log(2.0)).numpy()
+            assert np.max(np.abs(lse[b] - l2)) <= 1e-12
+
+
+def pin_head_map(ref):
+    """KV head g holds the constant V c_g; query head h must output c_(h // 8)."""
+    w = make_gqa(13, [20, 33], pool_pages=64)
+    v = w.v_pool.copy()
+    consts = [0.5, -1.25, 2.0, 3.5]
+    for g, c in enumerate(consts):
+        v[:, 0, g, :] = bf16_bits_from_f32(np.float32(c) * np.ones(w.head_dim, np.float32))
+    w.v_pool = v
+    out, _ = _decode(ref, w)
+    for h in range(w.num_qo_heads):
+        assert np.max(np.abs(out[:, h, :] - consts[h // 8])) <= 1e-14
+
+
+def pin_head_map_keys(ref):
+    """Only KV head g's keys may move query head h = 8g..8g+7: replace the keys
+    of every other KV head and the outputs of those 8 heads stay bit-equal."""
+    w = make_gqa(14, [25, 7], pool_pages=40)
+    out0, lse0 = _decode(ref, w)
+    for g in range(4):
+        k = w.k_pool.copy()
+        others = [x for x in range(4) if x != g]
+        k[:, 0, others, :] = k[::-1, 0, others, :]
+        w2 = make_gqa(14, [25, 7], pool_pages=40)
+        w2.k_pool = k
+        out1, lse1 = _decode(ref, w2)
+        heads = list(range(8 * g, 8 * g + 8))
+        assert np.array_equal(out0[:, heads], out1[:, heads])
+        assert np.array_equal(lse0[:, heads], lse1[:, heads])
+        rest = [h for h in range(32) if h not in heads]
+        assert not np.allclose(lse0[:, rest], lse1[:, rest])
+
+
+def pin_page_relabel(ref):
+    """Permuting the physical pages (and remapping the indices) changes nothing."""
+    w = _cfg("tiny")
+    out0, lse0 = _decode(ref, w)
+    rng = np.random.default_rng(99)
+    perm = rng.permutation(w.num_pages)
+    k = np.empty_like(w.k_pool)
+    v = np.empty_like(w.v_pool)
+    k[perm] = w.k_pool
+    v[perm] = w.v_pool
+    idx = perm[w.kv_indices].astype(np.int32)
+    out1, lse1 = ref.gqa_paged_decode(w.q, k, v, w.kv_indptr, idx, w.sm_scale)
+    assert np.array_equal(out0, out1) and np.array_equal(lse0, lse1)
+
+
+def pin_unused_pages_never_read(ref):
+    """NaN in the pages no sequence lists must not reach the result."""
+    w = _cfg("tiny")
+    used = np.zeros(w.num_pages, dtype=bool)
+    used[w.kv_indices] = True
+    k = w.k_pool.copy()
+    v = w.v_pool.copy()
+    k[~used] = 0x7FC0
+    v[~used] = 0x7FC0
+    out, lse = ref.gqa_paged_decode(w.q, k, v, w.kv_indptr, w.kv_indices, w.sm_scale)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+
+
+def pin_token_order(ref):
+    """Decode has no positions: reordering a sequence's page list changes only rounding."""
+    w = _small_edge()
+    out0, lse0 = _decode(ref, w)
+    rng = np.random.default_rng(7)
+    idx = w.kv_indices.copy()
+    for b in range(w.batch):
+        seg = idx[w.kv_indptr[b]:w.kv_indptr[b + 1]]
+        idx[w.kv_indptr[b]:w.kv_indptr[b + 1]] = seg[rng.permutation(len(seg))]
+    out1, lse1 = ref.gqa_paged_decode(w.q, w.k_pool, w.v_pool, w.kv_indptr, idx, w.sm_scale)
+    assert np.max(np.abs(out0 - out1)) <= 1e-12
+    fin = np.isfinite(lse0)
+    assert np.array_equal(fin, np.isfinite(lse1))
+    assert np.max(np.abs(lse0[fin] - lse1[fin])) <= 1e-12
+
+
+def pin_lse_bounds_and_convexity(ref):
+    """max_j s_j/ln2 <= lse <= max_j s_j/ln2 + log2 n; out lies in the V rows' hull."""
+    w = _small_edge()
+    out, lse = _decode(ref, w)
+    q = _f64(w.q)
+    for b in range(w.batch):
+        pages = w.kv_indices[w.kv_indptr[b]:w.kv_indptr[b + 1]]
+        if len(pages) == 0:
+            continue
+        for g in range(4):
+            k = _f64(w.k_pool[pages, 0, g])
+            v = _f64(w.v_pool[pages, 0, g])
+            for h in range(8 * g, 8 * g + 8):
+                smax = w.sm_scale * np.max(k @ q[b, h]) / math.log(2.0)
+                assert smax - 1e-12 <= lse[b, h] <= smax + math.log2(len(pages)) + 1e-12
+                assert np.all(out[b, h] >= v.min(axis=0) - 1e-12)
+                assert np.all(out[b, h] <= v.max(axis=0) + 1e-12)
+
+
+def pin_peaky(ref):
+    """Keys scaled by 30: the output sits on V of the best-scoring token."""
+    w = _small_edge()
+    b = 10
+    out, lse = _decode(ref, w, batches=[b])
+    pages = w.kv_indices[w.kv_indptr[b]:w.kv_indptr[b + 1]]
+    q = _f64(w.q[b])
+    hits = 0
+    for g in range(4):
+        k = _f64(w.k_pool[pages, 0, g])
+        v = _f64(w.v_pool[pages, 0, g])
+        for h in range(8 * g, 8 * g + 8):
+            s = w.sm_scale * (k @ q[h])
+            order = np.argsort(s)
+            gap = s[order[-1]] - s[order[-2]]
+            if gap > 40.0:   # every other weight is below e^-40
+                hits += 1
+                assert np.max(np.abs(out[b, h] - v[order[-1]])) <= 1e-12 * len(pages) + 1e-15
+                assert abs(lse[b, h] - s[order[-1]] / math.log(2.0)) <= 1e-12 * len(pages)
+    assert hits > 0
+
+
+# --------------------------------------------------------------- split/merge
+
+def pin_split_merge_identity(ref):
+    """Merging the partials of any partition equals the unsplit result."""
+    w = make_gqa(15, [300, 1, 77, 0, 129], pool_pages=600)
+    rng = np.random.default_rng(5)
+    full_out, full_lse = _decode(ref, w)
+    for b in range(w.batch):
+        n = int(w.lengths[b])
+        cuts = sorted(set([0, n] + [int(x) for x in rng.integers(0, n + 1, size=3)]))
+        cuts = [0] + cuts if cuts[0] != 0 else cuts
+        parts = [(cuts[i], cuts[i + 1]) for i in range(len(cuts) - 1)] + [(n, n)]
+        po, pl = [], []
+        for lo, hi in parts:
+            o, l_ = ref.gqa_decode_range(w.q, w.k_pool, w.v_pool, w.kv_indptr, w.kv_indices,
+                                         w.sm_scale, b, lo, hi)
+            po.append(o)
+            pl.append(l_)
+        mo, ml = ref.merge_lse2(np.stack(po), np.stack(pl))
+        assert np.max(np.abs(mo - full_out[b])) <= 1e-12
+        fin = np.isfinite(full_lse[b])
+        assert np.array_equal(fin, np.isfinite(ml))
+        if fin.any():
+            assert np.max(np.abs(ml[fin] - full_lse[b][fin])) <= 1e-12
+
+
+def pin_merge_closed_forms(ref):
+    """Two parts with equal LSE average; a -inf part is ignored; all -inf gives 0 / -inf."""
+    o = np.array([[[1.0, 2.0]], [[3.0, 6.0]]])
+    mo, ml = ref.merge_lse2(o, np.array([[5.0], [5.0]]))
+    assert np.allclose(mo, [[2.0, 4.0]], rtol=0, atol=1e-15) and abs(ml[0] - 6.0) <= 1e-15
+    mo, ml = ref.merge_lse2(o, np.array([[-np.inf], [1.5]]))
+    assert np.array_equal(mo, [[3.0, 6.0]]) and ml[0] == 1.5
+    mo, ml = ref.merge_lse2(o, np.array([[-np.inf], [-np.inf]]))
+    assert np.array_equal(mo, [[0.0, 0.0]]) and np.isneginf(ml[0])
+    # weights 2^0 and 2^-1 (base 2): (1*1 + 0.5*3) / 1.5
+    mo, ml = ref.merge_lse2(o, np.array([[2.0], [1.0]]))
+    assert abs(mo[0, 0] - 2.5 / 1.5) <= 1e-15 and abs(ml[0] - (2.0 + math.log2(1.5))) <= 1e-15
+
+
+# --------------------------------------------------------------- MLA gather
+
+def _small_mla():
+    if "small_mla" not in _CACHE:
+        _CACHE["small_mla"] = make_mla(21, batch=3, num_qo_heads=16, pool_tokens=300, topk=64,
+                                       masked_per_row=6)
+    return _CACHE["small_mla"]
+
+
+def pin_mla_masked_is_deleted(ref):
+    w = _small_mla()
+    out, lse = ref.mla_gather_decode(w.q, w.kv_pool, w.indices, w.sm_scale, w.d_v)
+    for b in range(w.batch):
+        kept = w.indices[b][w.indices[b] >= 0][None, :]
+        o1, l1 = ref.mla_gather_decode(w.q[b:b + 1], w.kv_pool, kept, w.sm_scale, w.d_v)
+        assert np.array_equal(out[b], o1[0]) and np.array_equal(lse[b], l1[0])
+    # an id past the pool end behaves like -1
+    idx = w.indices.copy()
+    idx[idx < 0] = w.pool_tokens + 17
+    o2, l2 = ref.mla_gather_decode(w.q, w.kv_pool, idx, w.sm_scale, w.d_v)
+    assert np.array_equal(out, o2) and np.array_equal(lse, l2)
+    # everything masked: zeros and -inf
+    o3, l3 = ref.mla_gather_decode(w.q, w.kv_pool, -np.ones_like(w.indices), w.sm_scale, w.d_v)
+    assert np.all(o3 == 0.0) and np.all(np.isneginf(l3))
+
+
+def pin_mla_sdpa(ref):
+    """Against torch SDPA: keys are the whole 576-wide row, values its first 512 dims."""
+    w = _small_mla()
+    out, lse = ref.mla_gather_decode(w.q, w.kv_pool, w.indices, w.sm_scale, w.d_v)
+    pool = torch.as_tensor(_f64(w.kv_pool))
+    for b in range(w.batch):
+        ids = torch.as_tensor(w.indices[b][w.indices[b] >= 0].astype(np.int64))
+        rows = pool[ids]                                   # [n, 576]
+        q = torch.as_tensor(_f64(w.q[b]))                  # [H, 576]
+        o = torch.nn.functional.scaled_dot_product_attention(
+            q[None, :, None, :], rows[None, None].expand(1, q.shape[0], -1, -1),
+            rows[None, None, :, :w.d_v].expand(1, q.shape[0], -1, -1), scale=w.sm_scale)
+        assert np.max(np.abs(out[b] - o[0, :, 0].numpy())) <= 1e-12
+        scores = w.sm_scale * (q @ rows.T)
+        l2 = (torch.logsumexp(scores, dim=-1) / math.log(2.0)).numpy()
+        assert np.max(np.abs(lse[b] - l2)) <= 1e-12
+
+
+def pin_mla_duplicates_count(ref):
+    """A repeated id counts twice: same as adding log2(2) weight to that row."""
+    w = _small_mla()
+    ids = np.array([[5, 9, 9, 200]], dtype=np.int32)
+    out, lse = ref.mla_gather_decode(w.q[:1], w.kv_pool, ids, w.sm_scale, w.d_v)
+    q = _f64(w.q[0])
+    rows = _f64(w.kv_pool[[5, 9, 200]])
+    s = w.sm_scale * (q @ rows.T)
+    e = np.exp(s) * np.array([1.0, 2.0, 1.0])
+    want = (e @ rows[:, :w.d_v]) / e.sum(axis=1, keepdims=True)
+    assert np.max(np.abs(out[0] - want)) <= 1e-12
+    assert np.max(np.abs(lse[0] - np.log2(e.sum(axis=1)))) <= 1e-12
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -1,0 +1,71 @@
+"""The seeded input generators: rounding, determinism and workload structure."""
+
+import hashlib
+
+import numpy as np
+import torch
+
+from inputs import bf16_bits_from_f32, lognormal_lengths, make_config
+from inputs.configs import EDGE_LENGTHS
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(100000).astype(np.float32) * 10,
+                        np.array([1.00390625, 1.01171875, -2.5, 0.0, -0.0, 1e-40, 3e38],
+                                 dtype=np.float32)])
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(bf16_bits_from_f32(x), want)
+    # ties go to even: 1 + 2^-8 sits halfway between 1 and 1 + 2^-7
+    assert bf16_bits_from_f32(np.array([1.00390625], np.float32))[0] == 0x3F80
+    assert bf16_bits_from_f32(np.array([1.01171875], np.float32))[0] == 0x3F82
+
+
+def _digest(w):
+    h = hashlib.sha256()
+    for a in (w.q, w.k_pool, w.v_pool, w.kv_indptr, w.kv_indices):
+        h.update(np.ascontiguousarray(a).tobytes())
+    return h.hexdigest()
+
+
+def test_determinism():
+    assert _digest(make_config("tiny")) == _digest(make_config("tiny"))
+
+
+def test_tiny_structure():
+    w = make_config("tiny")
+    assert list(w.lengths) == [17, 64] and w.num_pages == 128
+    assert len(set(w.kv_indices.tolist())) == 81
+    assert w.q.shape == (2, 32, 128) and w.k_pool.shape == (128, 1, 4, 128)
+    assert abs(w.sm_scale - 128 ** -0.5) < 1e-15
+
+
+def test_gqa_structure():
+    w = make_config("gqa")
+    assert w.batch == 64 and w.lengths.min() >= 512 and w.lengths.max() <= 4096
+    assert np.array_equal(np.sort(w.kv_indices), np.arange(w.total_tokens))
+
+
+def test_edge_structure():
+    w = make_config("edge")
+    assert tuple(w.lengths) == EDGE_LENGTHS and w.total_tokens == 69550
+    assert np.array_equal(np.sort(w.kv_indices), np.arange(69550))
+    pages = w.kv_indices[w.kv_indptr[7]:w.kv_indptr[8]]
+    assert np.all(w.v_pool[pages] == 0x3F40)      # 0.75
+
+
+def test_throughput_lengths():
+    n = lognormal_lengths(np.random.default_rng(4), 256)
+    assert n.min() >= 1 and n.max() <= 16384
+    assert 200_000 < n.sum() < 700_000
+
+
+def test_mla_structure():
+    w = make_config("mla")
+    assert w.q.shape == (32, 128, 576) and w.kv_pool.shape == (65536, 576)
+    assert w.indices.shape == (32, 2048)
+    for b in range(32):
+        row = w.indices[b]
+        assert int((row == -1).sum()) == 102
+        kept = row[row >= 0]
+        assert len(np.unique(kept)) == len(kept) and kept.max() < 65536

@@ -1,0 +1,61 @@
+"""Planted mistakes in a copy of the oracle must each fail at least one pin.
+
+The oracle's source is read, one plausible slip is written into the copy (a
+dropped term, a wrong sign, index or base, a transposed operand) and the copy
+is executed as a fresh module; the real oracle is never modified.
+"""
+
+import pathlib
+import types
+
+import pytest
+
+import pins
+
+SRC = (pathlib.Path(__file__).resolve().parents[1] / "oracle" / "ref.py").read_text()
+
+MUTANTS = {
+    "head_map_modulo": ("return head // (num_qo_heads // num_kv_heads)",
+                        "return head % num_kv_heads"),
+    "scale_dropped": ("s = sm_scale * (q @ k.T)", "s = (q @ k.T)"),
+    "scale_squared": ("s = sm_scale * (q @ k.T)", "s = sm_scale * sm_scale * (q @ k.T)"),
+    "lse_natural_log": ("lse = (m[:, 0] + np.log(z)) / LN2", "lse = (m[:, 0] + np.log(z))"),
+    "lse_max_dropped": ("lse = (m[:, 0] + np.log(z)) / LN2", "lse = np.log(z) / LN2"),
+    "not_normalised": ("out = (w @ v) / z[:, None]", "out = (w @ v)"),
+    "empty_lse_plus_inf": ("return np.zeros((h, v.shape[1])), np.full(h, -np.inf)",
+                           "return np.zeros((h, v.shape[1])), np.full(h, np.inf)"),
+    "k_head_zero": ("k = bf16_to_f64(k_bits[pages, 0, g, :])",
+                    "k = bf16_to_f64(k_bits[pages, 0, 0, :])"),
+    "v_from_k": ("v = bf16_to_f64(v_bits[pages, 0, g, :])",
+                 "v = bf16_to_f64(k_bits[pages, 0, g, :])"),
+    "bf16_shift": ("<< np.uint32(16)", "<< np.uint32(15)"),
+    "exp_sign": ("w = np.exp(s - m)", "w = np.exp(m - s)"),
+    "token_offset": ("pages = np.asarray(kv_indices[base + tok_begin: base + tok_end]",
+                     "pages = np.asarray(kv_indices[base + tok_begin + 1: base + tok_end + 1]"),
+    "merge_base_e": ("np.exp2(parts_lse - safe_top[None, :])",
+                     "np.exp(parts_lse - safe_top[None, :])"),
+    "merge_lse_no_log": ("safe_top + np.log2(np.where(empty, 1.0, den))", "safe_top"),
+    "mla_upper_mask_dropped": ("ids = ids[(ids >= 0) & (ids < pool_tokens)]",
+                               "ids = ids[(ids >= 0)]"),
+    "mla_v_tail": ("rows[:, :d_v]", "rows[:, -d_v:]"),
+    "scores_transposed_q": ("s = sm_scale * (q @ k.T)", "s = sm_scale * (q[::-1] @ k.T)"),
+}
+
+
+def _load_mutant(old, new):
+    assert SRC.count(old) == 1, f"mutation anchor not unique: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(SRC.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    mod = _load_mutant(*MUTANTS[name])
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(mod)
+        except Exception:  # AssertionError or a crash both count as caught
+            caught.append(pin.__name__)
+    assert caught, f"no pin fails for mutant {name}"

@@ -1,0 +1,226 @@
+"""Paged GQA decode bench (one MI355X).
+
+One step is one full hot-path call: pkv_run (partial decode of every work
+item) plus pkv_merge (LSE merge of split sequences) over one batch. Inputs are
+resident in HBM before timing starts. To keep the 256 MB Infinity Cache from
+serving repeated reads of the same pool, the K/V pools are replicated and the
+steps rotate over the replicas (each replica is a separate allocation with the
+same contents), so every step streams its pool from HBM.
+
+Prints one JSON line. `value` is the KV-read bandwidth (2048 bytes per token:
+4 KV heads x 128 dims x 2 bytes for K and again for V) over the wall time of
+the timed steps. `roofline` rates the decode kernel alone: its algorithmic
+bytes per launch over its average launch time from HIP events on the stream it
+runs on. `cpu_baseline` times the fp64 CPU oracle on the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "achieved KV-read HBM GB/s (% of peak) + µs/call, GQA h32/kv4/d128 decode"
+WORKLOAD_TEXT = {
+    "tiny": "paged GQA decode, B=2, seq_lens {17,64}, h_q=32 h_kv=4 d=128 page_size=1",
+    "gqa": "paged GQA decode, B=64, seq_lens uniform [512,4096], h_q=32 h_kv=4 d=128 page_size=1, "
+           "pool = sum(seq_lens) pages randomly permuted",
+    "edge": "paged GQA decode, B=16 edge-case seq_lens (0..32768), h_q=32 h_kv=4 d=128 page_size=1",
+    "throughput": "paged GQA decode, B=256, seq_lens log-normal (median 1024, sigma 1, clip "
+                  "[1,16384]), h_q=32 h_kv=4 d=128 page_size=1, split-KV",
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partial_gqa_traffic.txt")
+KERNEL_SRC = os.path.join(ROOT, "paged_kv_attention_gqa_amd", "csrc", "decode.hip")
+
+
+def algorithmic_decode_bytes(w, plan_flat) -> int:
+    """Bytes the decode kernel must move per launch (each byte once).
+
+    Per token: 2048 B of K/V rows + 4 B page id. Per sequence: 8192 B of q and
+    the 4-byte indptr entry. Per directly written sequence: 8192 B bf16 out +
+    128 B lse. Per split chunk: 16384 B fp32 partial + 128 B partial LSE. Plus
+    16 B per work item of plan table.
+    """
+    _, n_items, n_merges, n_slots = plan_flat[:4]
+    items = np.array(plan_flat[4:4 + 4 * n_items], dtype=np.int64).reshape(-1, 4)
+    direct = int(np.sum(items[:, 3] < 0))
+    n = w.total_tokens
+    return (2052 * n + 8192 * w.batch + 4 * (w.batch + 1) + direct * (8192 + 128)
+            + n_slots * (16384 + 128) + 16 * n_items)
+
+
+def read_traffic(kernel_src: str):
+    """HBM bytes per launch from the committed counter summary, or None if the
+    kernel source has changed since the counters were taken."""
+    import hashlib
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    if vals.get("kernel_source_sha256") != sha:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, budget_s: float):
+    """Time the fp64 oracle on the whole batch, repeated until ~budget_s of CPU work."""
+    from oracle import ref
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    reps, t_total = 0, 0.0
+    while t_total < budget_s and reps < 50:
+        t0 = time.perf_counter()
+        ref.gqa_paged_decode(w.q, w.k_pool, w.v_pool, w.kv_indptr, w.kv_indices, w.sm_scale)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    per_call = t_total / reps
+    return {"value": 2048.0 * w.total_tokens / per_call / 1e9, "unit": "GB/s", "cores": cores,
+            "kind": "oracle", "us_per_call": per_call * 1e6,
+            "sample": f"whole batch ({w.batch} sequences, {w.total_tokens} tokens), {reps} runs, "
+                      f"{t_total:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="gqa", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--replicas", type=int, default=0, help="pool copies to rotate (0 = auto)")
+    ap.add_argument("--no-split", action="store_true")
+    ap.add_argument("--chunk", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration runs)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_attention_gqa_amd as pkv
+    from inputs import make_config
+
+    dev = torch.device("cuda:0")
+    w = make_config(args.config)
+    as_t = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    q = as_t(w.q)
+    pool_bytes = 2 * w.k_pool.nbytes
+    reps = args.replicas or max(1, min(8, math.ceil(768e6 / max(pool_bytes, 1)) + 1))
+    k0, v0 = as_t(w.k_pool), as_t(w.v_pool)
+    pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(reps - 1)]
+    indptr = torch.from_numpy(w.kv_indptr).to(dev)
+    indices = torch.from_numpy(w.kv_indices).to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+
+    t0 = time.perf_counter()
+    ws_bytes = pkv.pkv_workspace_size(w.kv_indptr, allow_split=not args.no_split,
+                                      chunk_tokens=args.chunk)
+    plan_us = (time.perf_counter() - t0) * 1e6
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    plan = pkv.pkv_plan_create(w.kv_indptr, allow_split=not args.no_split,
+                               chunk_tokens=args.chunk, workspace=ws)
+    flat = pkv.pkv_plan_export(plan)
+    torch.cuda.synchronize()
+
+    def step(i):
+        k, v = pools[i % reps]
+        pkv.pkv_run(plan, q, k, v, indptr, indices, w.sm_scale, ws, out, lse)
+        pkv.pkv_merge(plan, ws, out, lse)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        k, v = pools[i % reps]
+        ev[i][0].record(stream)
+        pkv.pkv_run(plan, q, k, v, indptr, indices, w.sm_scale, ws, out, lse)
+        ev[i][1].record(stream)
+        pkv.pkv_merge(plan, ws, out, lse)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    if args.calib_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    decode_ms = np.array([s.elapsed_time(e) for s, e in ev])
+    decode_s = float(decode_ms.mean()) / 1e3
+    kv_bytes = 2048.0 * w.total_tokens
+    ms_per_step = wall / args.steps * 1e3
+    value = kv_bytes / (wall / args.steps) / 1e9
+    alg = algorithmic_decode_bytes(w, flat)
+    achieved = alg / decode_s / 1e9
+    traffic = read_traffic(KERNEL_SRC)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_call": round(ms_per_step * 1e3, 2),
+        "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "decode_tokens_per_s": round(w.batch / (wall / args.steps), 1),
+        "kv_tokens_per_s": round(w.total_tokens / (wall / args.steps), 1),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 q/K/V, random page permutation)",
+        "config": {"workload": WORKLOAD_TEXT[args.config], "name": args.config,
+                   "batch": w.batch, "total_tokens": w.total_tokens,
+                   "split": not args.no_split, "chunk_tokens": flat[0], "work_items": flat[1],
+                   "split_sequences": flat[2], "pool_replicas": reps,
+                   "plan_host_us": round(plan_us, 1)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": traffic, "kernel": "decode_partial_kernel",
+                     "kernel_avg_us": round(decode_s * 1e6, 3),
+                     "kernel_p10_us": round(float(np.percentile(decode_ms, 10)) * 1e3, 3),
+                     "kernel_p90_us": round(float(np.percentile(decode_ms, 90)) * 1e3, 3),
+                     "algorithmic_bytes_per_launch": alg},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

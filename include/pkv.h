@@ -1,0 +1,167 @@
+/*
+ * pkv — single-token paged attention decode for AMD MI355X (gfx950).
+ *
+ * C ABI of the library libpkv.so. Every entry point returns a pkv_status
+ * (PKV_OK == 0); on failure pkv_last_error() gives a thread-local message.
+ * No entry point allocates device memory or synchronises: run, merge and
+ * gather only enqueue kernels on the caller's HIP stream. The caller owns every
+ * device buffer (inputs, outputs, workspace); the library owns only the host
+ * plan object.
+ *
+ * What is computed (paged GQA decode; kernelindex.com, "flashinfer
+ * gemini-2.5-pro / triton h7ykt0", kernel gqa_paged_decode_h32_kv4_d128_ps1,
+ * steps 2-9, and its wrapper run()): for sequence b with n = indptr[b+1] -
+ * indptr[b] tokens, token j stored in page p_j = kv_indices[kv_indptr[b] + j],
+ * and query head h reading KV head g = h / (Hq / Hkv):
+ *
+ *     s_j      = sm_scale * dot(q[b,h,:], K[p_j, 0, g, :])
+ *     out[b,h] = sum_j exp(s_j) V[p_j, 0, g, :] / sum_j exp(s_j)   (bf16)
+ *     lse[b,h] = log2(sum_j exp(s_j))                               (fp32)
+ *
+ * and out = 0, lse = -inf when n == 0. Long sequences are split into chunks
+ * whose normalised fp32 partials and base-2 LSEs are combined by pkv_merge
+ * (vLLM fork qsa.py, _qsa_sparse_paged_gqa_splitk_kernel and
+ * _qsa_merge_splitk_kernel).
+ *
+ * Supported shapes (compiled in): Hq = 32, Hkv = 4, head_dim = 128,
+ * page_size = 1, bf16 q/K/V. Other shapes return PKV_ERR_UNSUPPORTED.
+ *
+ * Layouts (all contiguous, row-major; bf16 as 16-bit patterns; device
+ * pointers 16-byte aligned):
+ *   q        bf16  [B, Hq, D]
+ *   k_pool   bf16  [num_pages, page_size, Hkv, D]   (v_pool the same)
+ *   kv_indptr int32 [B + 1]   (device copy; the plan reads a host copy)
+ *   kv_indices int32 [kv_indptr[B]], each in [0, num_pages)  (caller
+ *            precondition, as in the page's kernel: not checked on device)
+ *   out      bf16  [B, Hq, D]
+ *   lse      fp32  [B, Hq], base 2
+ */
+#ifndef PKV_H_
+#define PKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = 1,         /* null pointer, bad length, misaligned, non-finite scale */
+  PKV_ERR_UNSUPPORTED = 2,         /* heads / dim / page size not compiled in */
+  PKV_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes below what the plan needs */
+  PKV_ERR_PLAN_MISMATCH = 4,       /* call does not match the plan it names */
+  PKV_ERR_HIP = 5                  /* a HIP runtime call or launch failed */
+} pkv_status;
+
+/* Opaque host object: the split-KV work partition of one batch. */
+typedef struct pkv_plan pkv_plan;
+
+/*
+ * Bytes of device workspace a plan of this batch needs (work tables plus the
+ * fp32 partials of split sequences). Same arguments as pkv_plan_create.
+ * kv_indptr_host: host int32 [batch + 1], non-decreasing, kv_indptr_host[0] == 0.
+ * num_cus: compute units to plan for; 0 queries the current HIP device.
+ * allow_split: 0 keeps every sequence in one work item (no merge needed).
+ * chunk_tokens: chunk length override (rounded up to 32); 0 chooses it from
+ * the total token count and num_cus.
+ */
+pkv_status pkv_workspace_size(const int32_t* kv_indptr_host, int32_t batch,
+                              int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t page_size, int32_t num_cus, int32_t allow_split,
+                              int32_t chunk_tokens, size_t* bytes);
+
+/*
+ * Build the split-KV partition of a batch (host work, O(batch)) and, when
+ * `workspace` is non-NULL, enqueue the upload of its work tables into the
+ * workspace on `stream` (a hipStream_t; NULL is the default stream). The
+ * workspace must then be passed unchanged to pkv_run and pkv_merge; a NULL
+ * workspace gives a host-only plan that can be exported but not run. The
+ * plan records the batch shape; later calls that differ return
+ * PKV_ERR_PLAN_MISMATCH (the plan-capture rule of the FlagGems
+ * flash_mla_with_kvcache page, FlashMLASchedMeta). The caller keeps the device
+ * kv_indptr equal to the host copy given here.
+ * On success *plan receives a new object, freed with pkv_plan_destroy.
+ */
+pkv_status pkv_plan_create(const int32_t* kv_indptr_host, int32_t batch,
+                           int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t page_size, int32_t num_cus, int32_t allow_split,
+                           int32_t chunk_tokens, void* workspace, size_t workspace_bytes,
+                           void* stream, pkv_plan** plan);
+
+/* Frees a plan (NULL is ignored). Does not touch device memory. */
+void pkv_plan_destroy(pkv_plan* plan);
+
+/*
+ * Copy the plan's integer tables to host memory:
+ * [chunk, n_items, n_merges, n_slots], then n_items records
+ * (b, tok_begin, tok_end, slot) with slot -1 for a sequence written directly,
+ * then n_merges records (b, first_slot, n_chunks, 0). *needed receives the
+ * count of int32 values; dst may be NULL to query it. Fails with
+ * PKV_ERR_INVALID_ARG when n_int32 is smaller than that count.
+ */
+pkv_status pkv_plan_export(const pkv_plan* plan, int32_t* dst, size_t n_int32, size_t* needed);
+
+/*
+ * Enqueue the partial-decode kernel for every work item of the plan. Sequences
+ * in one chunk get their final out/lse; split sequences get fp32 partials in
+ * the workspace, finished by pkv_merge. Shapes are passed so that they can be
+ * checked against the plan: q is [q_batch, q_heads, q_dim], each pool is
+ * [num_pages, page_size, pool_kv_heads, pool_dim], kv_indptr has indptr_len
+ * entries and kv_indices has num_indices entries (must equal the plan's
+ * kv_indptr[B]). sm_scale must be finite (the Python layer fills the default
+ * 1/sqrt(head_dim)).
+ */
+pkv_status pkv_run(const pkv_plan* plan,
+                   const void* q, int32_t q_batch, int32_t q_heads, int32_t q_dim,
+                   const void* k_pool, const void* v_pool, int64_t num_pages,
+                   int32_t page_size, int32_t pool_kv_heads, int32_t pool_dim,
+                   const int32_t* kv_indptr, int64_t indptr_len,
+                   const int32_t* kv_indices, int64_t num_indices,
+                   float sm_scale, void* workspace, size_t workspace_bytes,
+                   void* out, float* lse, void* stream);
+
+/*
+ * Enqueue the LSE merge of split sequences (a no-op when the plan split
+ * nothing): lse* = max_i lse_i, w_i = 2^(lse_i - lse*),
+ * out = sum_i w_i o_i / sum_i w_i, lse = lse* + log2(sum_i w_i).
+ * Must follow pkv_run on the same stream with the same workspace.
+ */
+pkv_status pkv_merge(const pkv_plan* plan, void* workspace, size_t workspace_bytes,
+                     void* out, float* lse, void* stream);
+
+/*
+ * Index-gather latent-attention decode (FlagGems flash_mla_with_kvcache page,
+ * _sparse_decode_kernel in its bf16 mode). Row b attends to the pool rows
+ * kv_pool[t] for every entry t = indices[b, i] with 0 <= t < pool_tokens;
+ * other entries (e.g. -1) are masked and contribute nothing. Scores use all
+ * d_qk dims; values are the first d_v dims of the same row:
+ *     out[b,h] = sum_t exp(s_t) kv[t, :d_v] / sum_t exp(s_t),
+ *     s_t = sm_scale * dot(q[b,h,:], kv[t,:]),   lse[b,h] = log2 sum_t exp(s_t)
+ * and out = 0, lse = -inf when no entry is valid.
+ * Layouts: q bf16 [batch, num_qo_heads, d_qk]; kv_pool bf16 [pool_tokens, d_qk];
+ * indices int32 [batch, topk]; out bf16 [batch, num_qo_heads, d_v];
+ * lse fp32 [batch, num_qo_heads]. Compiled for d_qk = 576, d_v = 512 and
+ * num_qo_heads a multiple of 16 up to 128. workspace: device scratch of
+ * pkv_gather_mla_workspace_size bytes.
+ */
+pkv_status pkv_gather_mla_workspace_size(int32_t batch, int32_t num_qo_heads, int32_t d_qk,
+                                         int32_t d_v, int32_t topk, size_t* bytes);
+pkv_status pkv_gather_mla(const void* q, const void* kv_pool, int64_t pool_tokens,
+                          const int32_t* indices, int32_t topk, int32_t batch,
+                          int32_t num_qo_heads, int32_t d_qk, int32_t d_v, float sm_scale,
+                          void* workspace, size_t workspace_bytes, void* out, float* lse,
+                          void* stream);
+
+/* Static text for a status code. */
+const char* pkv_status_string(pkv_status status);
+
+/* Detail of the last failure on this thread ("" if none). */
+const char* pkv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H_ */

@@ -1,0 +1,304 @@
+"""Python binding of libpkv (paged KV-cache attention decode for MI355X).
+
+Argument marshalling only: every function here turns torch tensors into
+pointers and sizes and calls the C entry point of the same name declared in
+``include/pkv.h``. All computation happens in the library's HIP kernels. The
+library is loaded on first use; if it has not been built, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import numpy as np
+
+from ._build import LIB_PATH
+
+__all__ = [
+    "PkvError", "Plan", "decode", "gather_mla", "library_path",
+    "pkv_workspace_size", "pkv_plan_create", "pkv_plan_destroy", "pkv_plan_export",
+    "pkv_run", "pkv_merge", "pkv_gather_mla_workspace_size", "pkv_gather_mla",
+    "pkv_status_string", "pkv_last_error",
+]
+
+PKV_OK = 0
+PKV_ERR_INVALID_ARG = 1
+PKV_ERR_UNSUPPORTED = 2
+PKV_ERR_WORKSPACE_TOO_SMALL = 3
+PKV_ERR_PLAN_MISMATCH = 4
+PKV_ERR_HIP = 5
+
+# Every symbol include/pkv.h declares, with (restype, argtypes).
+_c = ctypes
+_P = _c.c_void_p
+_I32 = _c.c_int32
+_I64 = _c.c_int64
+_SZ = _c.c_size_t
+_I32P = _c.POINTER(_c.c_int32)
+SIGNATURES = {
+    "pkv_workspace_size": (_I32, [_I32P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                  _c.POINTER(_SZ)]),
+    "pkv_plan_create": (_I32, [_I32P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _SZ,
+                               _P, _c.POINTER(_P)]),
+    "pkv_plan_destroy": (None, [_P]),
+    "pkv_plan_export": (_I32, [_P, _I32P, _SZ, _c.POINTER(_SZ)]),
+    "pkv_run": (_I32, [_P, _P, _I32, _I32, _I32, _P, _P, _I64, _I32, _I32, _I32, _P, _I64, _P,
+                       _I64, _c.c_float, _P, _SZ, _P, _P, _P]),
+    "pkv_merge": (_I32, [_P, _P, _SZ, _P, _P, _P]),
+    "pkv_gather_mla_workspace_size": (_I32, [_I32, _I32, _I32, _I32, _I32, _c.POINTER(_SZ)]),
+    "pkv_gather_mla": (_I32, [_P, _P, _I64, _P, _I32, _I32, _I32, _I32, _I32, _c.c_float, _P,
+                              _SZ, _P, _P, _P]),
+    "pkv_status_string": (_c.c_char_p, [_I32]),
+    "pkv_last_error": (_c.c_char_p, []),
+}
+
+_LIB = None
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def lib():
+    """The loaded libpkv (ctypes). Raises if the library has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libpkv.so is not built ({LIB_PATH}); run "
+                               "paged_kv_attention_gqa_amd._build.build() first")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = handle
+    return _LIB
+
+
+class PkvError(Exception):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        detail = lib().pkv_last_error().decode()
+        text = lib().pkv_status_string(status).decode()
+        super().__init__(f"{where}: {text} ({status}): {detail}")
+
+
+class PkvValueError(PkvError, ValueError):
+    pass
+
+
+class PkvRuntimeError(PkvError, RuntimeError):
+    pass
+
+
+def _check(status: int, where: str):
+    if status != PKV_OK:
+        raise (PkvRuntimeError if status == PKV_ERR_HIP else PkvValueError)(status, where)
+
+
+def pkv_status_string(status: int) -> str:
+    return lib().pkv_status_string(status).decode()
+
+
+def pkv_last_error() -> str:
+    return lib().pkv_last_error().decode()
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def _stream(stream) -> int:
+    if stream is not None:
+        return int(stream)
+    import torch
+    return int(torch.cuda.current_stream().cuda_stream)
+
+
+def _host_indptr(kv_indptr_host) -> np.ndarray:
+    if hasattr(kv_indptr_host, "detach"):
+        kv_indptr_host = kv_indptr_host.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(kv_indptr_host), dtype=np.int32)
+
+
+def _require(t, name, dtypes, cuda=True):
+    import torch
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if cuda and t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+
+
+def _bf16_types():
+    import torch
+    return (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def pkv_workspace_size(kv_indptr_host, num_qo_heads=32, num_kv_heads=4, head_dim=128,
+                       page_size=1, num_cus=0, allow_split=True, chunk_tokens=0) -> int:
+    ind = _host_indptr(kv_indptr_host)
+    out = ctypes.c_size_t(0)
+    _check(lib().pkv_workspace_size(ind.ctypes.data_as(_I32P), len(ind) - 1, num_qo_heads,
+                                    num_kv_heads, head_dim, page_size, num_cus,
+                                    int(bool(allow_split)), chunk_tokens, ctypes.byref(out)),
+           "pkv_workspace_size")
+    return int(out.value)
+
+
+class Plan:
+    """Owns one pkv_plan handle (destroyed with the object)."""
+
+    def __init__(self, handle: int, batch: int, total_tokens: int):
+        self.handle = handle
+        self.batch = batch
+        self.total_tokens = total_tokens
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _LIB is not None:
+            _LIB.pkv_plan_destroy(self.handle)
+            self.handle = None
+
+
+def pkv_plan_create(kv_indptr_host, num_qo_heads=32, num_kv_heads=4, head_dim=128, page_size=1,
+                    num_cus=0, allow_split=True, chunk_tokens=0, workspace=None,
+                    stream=None) -> Plan:
+    ind = _host_indptr(kv_indptr_host)
+    if workspace is not None:
+        _require(workspace, "workspace", (__import__("torch").uint8,))
+    handle = ctypes.c_void_p(0)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    st = 0 if workspace is None else _stream(stream)
+    _check(lib().pkv_plan_create(ind.ctypes.data_as(_I32P), len(ind) - 1, num_qo_heads,
+                                 num_kv_heads, head_dim, page_size, num_cus,
+                                 int(bool(allow_split)), chunk_tokens, _ptr(workspace), ws_bytes,
+                                 st, ctypes.byref(handle)),
+           "pkv_plan_create")
+    return Plan(handle.value, len(ind) - 1, int(ind[-1]) if len(ind) else 0)
+
+
+def pkv_plan_destroy(plan: Plan):
+    if plan.handle:
+        lib().pkv_plan_destroy(plan.handle)
+        plan.handle = None
+
+
+def pkv_plan_export(plan: Plan) -> list:
+    need = ctypes.c_size_t(0)
+    _check(lib().pkv_plan_export(plan.handle, None, 0, ctypes.byref(need)), "pkv_plan_export")
+    buf = (ctypes.c_int32 * need.value)()
+    _check(lib().pkv_plan_export(plan.handle, buf, need.value, ctypes.byref(need)),
+           "pkv_plan_export")
+    return list(buf)
+
+
+def pkv_run(plan: Plan, q, k_pool, v_pool, kv_indptr, kv_indices, sm_scale, workspace, out,
+            lse, stream=None):
+    import torch
+    bf = _bf16_types()
+    _require(q, "q", bf)
+    _require(k_pool, "k_pool", bf)
+    _require(v_pool, "v_pool", bf)
+    _require(kv_indptr, "kv_indptr", (torch.int32,))
+    _require(kv_indices, "kv_indices", (torch.int32,))
+    _require(workspace, "workspace", (torch.uint8,))
+    _require(out, "out", bf)
+    _require(lse, "lse", (torch.float32,))
+    if q.dim() != 3 or k_pool.dim() != 4:
+        raise ValueError("q must be [B, Hq, D] and the pools [pages, page_size, Hkv, D]")
+    if tuple(k_pool.shape) != tuple(v_pool.shape):
+        raise ValueError("k_pool and v_pool must have the same shape")
+    if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != tuple(q.shape[:2]):
+        raise ValueError("out must be shaped like q and lse like q.shape[:2]")
+    _check(lib().pkv_run(plan.handle, _ptr(q), q.shape[0], q.shape[1], q.shape[2], _ptr(k_pool),
+                         _ptr(v_pool), k_pool.shape[0], k_pool.shape[1], k_pool.shape[2],
+                         k_pool.shape[3], _ptr(kv_indptr), kv_indptr.numel(), _ptr(kv_indices),
+                         kv_indices.numel(), float(sm_scale), _ptr(workspace), workspace.numel(),
+                         _ptr(out), _ptr(lse), _stream(stream)),
+           "pkv_run")
+
+
+def pkv_merge(plan: Plan, workspace, out, lse, stream=None):
+    _check(lib().pkv_merge(plan.handle, _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse),
+                           _stream(stream)),
+           "pkv_merge")
+
+
+def pkv_gather_mla_workspace_size(batch, num_qo_heads, d_qk, d_v, topk) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().pkv_gather_mla_workspace_size(batch, num_qo_heads, d_qk, d_v, topk,
+                                               ctypes.byref(out)),
+           "pkv_gather_mla_workspace_size")
+    return int(out.value)
+
+
+def pkv_gather_mla(q, kv_pool, indices, sm_scale, workspace, out, lse, d_v=512, stream=None):
+    import torch
+    bf = _bf16_types()
+    _require(q, "q", bf)
+    _require(kv_pool, "kv_pool", bf)
+    _require(indices, "indices", (torch.int32,))
+    _require(workspace, "workspace", (torch.uint8,))
+    _require(out, "out", bf)
+    _require(lse, "lse", (torch.float32,))
+    if q.dim() != 3 or kv_pool.dim() != 2 or indices.dim() != 2:
+        raise ValueError("q must be [B, Hq, Dqk], kv_pool [T, Dqk], indices [B, topk]")
+    if kv_pool.shape[1] != q.shape[2] or indices.shape[0] != q.shape[0]:
+        raise ValueError("kv_pool width must equal q's and indices must have one row per query")
+    if tuple(out.shape) != (q.shape[0], q.shape[1], d_v) or tuple(lse.shape) != tuple(q.shape[:2]):
+        raise ValueError("out must be [B, Hq, d_v] and lse [B, Hq]")
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    _check(lib().pkv_gather_mla(_ptr(q), _ptr(kv_pool), kv_pool.shape[0], _ptr(indices),
+                                indices.shape[1], q.shape[0], q.shape[1], q.shape[2], d_v,
+                                float(sm_scale), _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse),
+                                _stream(stream)),
+           "pkv_gather_mla")
+
+
+# ------------------------------------------------------------ conveniences
+
+def decode(q, k_pool, v_pool, kv_indptr, kv_indices, sm_scale: Optional[float] = None,
+           kv_indptr_host=None, allow_split=True, chunk_tokens=0, num_cus=0, stream=None):
+    """Plan, run and merge one paged GQA decode; returns ``(out, lse)`` (bf16, fp32 base 2).
+
+    ``sm_scale`` defaults to 1/sqrt(head_dim). ``kv_indptr_host`` (a host copy
+    of ``kv_indptr``) avoids a device-to-host copy when given.
+    """
+    import torch
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(q.shape[-1])
+    if kv_indptr_host is None:
+        kv_indptr_host = kv_indptr.cpu()
+    ws_bytes = pkv_workspace_size(kv_indptr_host, q.shape[1], k_pool.shape[2], q.shape[2],
+                                  k_pool.shape[1], num_cus, allow_split, chunk_tokens)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    plan = pkv_plan_create(kv_indptr_host, q.shape[1], k_pool.shape[2], q.shape[2],
+                           k_pool.shape[1], num_cus, allow_split, chunk_tokens, ws, stream)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    pkv_run(plan, q, k_pool, v_pool, kv_indptr, kv_indices, sm_scale, ws, out, lse, stream)
+    pkv_merge(plan, ws, out, lse, stream)
+    return out, lse
+
+
+def gather_mla(q, kv_pool, indices, sm_scale: Optional[float] = None, d_v: int = 512,
+               stream=None):
+    """Index-gather latent decode; returns ``(out [B, Hq, d_v], lse [B, Hq])``."""
+    import torch
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(q.shape[-1])
+    ws_bytes = pkv_gather_mla_workspace_size(q.shape[0], q.shape[1], q.shape[2], d_v,
+                                             indices.shape[1])
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    out = torch.empty((q.shape[0], q.shape[1], d_v), dtype=q.dtype, device=q.device)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    pkv_gather_mla(q, kv_pool, indices, sm_scale, ws, out, lse, d_v, stream)
+    return out, lse

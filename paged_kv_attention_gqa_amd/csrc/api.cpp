@@ -1,0 +1,331 @@
+// C ABI of libpkv: argument checks, the plan object, workspace layout and
+// kernel launches. Every check runs on the host before any HIP call, so a
+// rejected call has no effect on the device.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/pkv.h"
+#include "kernels.h"
+#include "mla.h"
+#include "plan.h"
+
+struct pkv_plan {
+  int32_t batch;
+  int32_t num_qo_heads, num_kv_heads, head_dim, page_size;
+  int32_t num_cus, allow_split;
+  pkv::Partition part;
+  std::vector<int32_t> tables;   // items then merge records, as uploaded
+  size_t off_items, off_merges, off_part_o, off_part_lse, ws_bytes;
+  void* workspace;               // device buffer the tables were uploaded to (or NULL)
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pkv_status fail(pkv_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+pkv_status ok() {
+  g_last_error.clear();
+  return PKV_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+pkv_status check_gqa_shape(int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t page_size) {
+  if (num_qo_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || page_size <= 0)
+    return fail(PKV_ERR_INVALID_ARG, "head counts, head_dim and page_size must be positive");
+  if (num_qo_heads % num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_qo_heads (%d) must be a multiple of num_kv_heads (%d)",
+                num_qo_heads, num_kv_heads);
+  if (num_qo_heads != pkv::kHq)
+    return fail(PKV_ERR_UNSUPPORTED, "expected num_qo_heads=%d, got %d", pkv::kHq, num_qo_heads);
+  if (num_kv_heads != pkv::kHkv)
+    return fail(PKV_ERR_UNSUPPORTED, "expected num_kv_heads=%d, got %d", pkv::kHkv, num_kv_heads);
+  if (head_dim != pkv::kHeadDim)
+    return fail(PKV_ERR_UNSUPPORTED, "expected head_dim=%d, got %d", pkv::kHeadDim, head_dim);
+  if (page_size != 1)
+    return fail(PKV_ERR_UNSUPPORTED, "expected page_size=1, got %d", page_size);
+  return PKV_OK;
+}
+
+pkv_status resolve_cus(int32_t* num_cus) {
+  if (*num_cus > 0) return PKV_OK;
+  if (*num_cus < 0) return fail(PKV_ERR_INVALID_ARG, "num_cus must be >= 0");
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  int cus = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "hipDeviceGetAttribute: %s", hipGetErrorString(e));
+  *num_cus = cus;
+  return PKV_OK;
+}
+
+// Builds the partition and the workspace layout of a plan (no device work).
+pkv_status make_plan(const int32_t* kv_indptr_host, int32_t batch, int32_t num_qo_heads,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t num_cus,
+                     int32_t allow_split, int32_t chunk_tokens, pkv_plan* p) {
+  if (kv_indptr_host == nullptr) return fail(PKV_ERR_INVALID_ARG, "kv_indptr_host is NULL");
+  if (batch < 0) return fail(PKV_ERR_INVALID_ARG, "batch must be >= 0");
+  pkv_status s = check_gqa_shape(num_qo_heads, num_kv_heads, head_dim, page_size);
+  if (s != PKV_OK) return s;
+  if (chunk_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "chunk_tokens must be >= 0");
+  s = resolve_cus(&num_cus);
+  if (s != PKV_OK) return s;
+  std::string err;
+  if (!pkv::build_partition(kv_indptr_host, batch, num_cus, allow_split != 0, chunk_tokens,
+                            &p->part, &err))
+    return fail(PKV_ERR_INVALID_ARG, "%s", err.c_str());
+  p->batch = batch;
+  p->num_qo_heads = num_qo_heads;
+  p->num_kv_heads = num_kv_heads;
+  p->head_dim = head_dim;
+  p->page_size = page_size;
+  p->num_cus = num_cus;
+  p->allow_split = allow_split != 0;
+  p->tables.clear();
+  p->tables.reserve(4 * (p->part.items.size() + p->part.merges.size()));
+  for (const auto& it : p->part.items) {
+    p->tables.insert(p->tables.end(), {it.b, it.tok_begin, it.tok_end, it.slot});
+  }
+  for (const auto& m : p->part.merges) {
+    p->tables.insert(p->tables.end(), {m.b, m.first_slot, m.n_chunks, m.pad});
+  }
+  const size_t slots = static_cast<size_t>(p->part.n_slots);
+  p->off_items = 0;
+  p->off_merges = p->off_items + 16 * p->part.items.size();
+  p->off_part_o = align_up(p->off_merges + 16 * p->part.merges.size());
+  p->off_part_lse = align_up(p->off_part_o + slots * num_qo_heads * head_dim * sizeof(float));
+  p->ws_bytes = align_up(p->off_part_lse + slots * num_qo_heads * sizeof(float));
+  p->workspace = nullptr;
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_status_string(pkv_status status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_INVALID_ARG: return "invalid argument";
+    case PKV_ERR_UNSUPPORTED: return "unsupported shape";
+    case PKV_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case PKV_ERR_PLAN_MISMATCH: return "call does not match the plan";
+    case PKV_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* pkv_last_error(void) { return g_last_error.c_str(); }
+
+pkv_status pkv_workspace_size(const int32_t* kv_indptr_host, int32_t batch, int32_t num_qo_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                              int32_t num_cus, int32_t allow_split, int32_t chunk_tokens,
+                              size_t* bytes) {
+  if (bytes == nullptr) return fail(PKV_ERR_INVALID_ARG, "bytes is NULL");
+  pkv_plan p;
+  pkv_status s = make_plan(kv_indptr_host, batch, num_qo_heads, num_kv_heads, head_dim,
+                           page_size, num_cus, allow_split, chunk_tokens, &p);
+  if (s != PKV_OK) return s;
+  *bytes = p.ws_bytes;
+  return ok();
+}
+
+pkv_status pkv_plan_create(const int32_t* kv_indptr_host, int32_t batch, int32_t num_qo_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                           int32_t num_cus, int32_t allow_split, int32_t chunk_tokens,
+                           void* workspace, size_t workspace_bytes, void* stream,
+                           pkv_plan** plan) {
+  if (plan == nullptr) return fail(PKV_ERR_INVALID_ARG, "plan is NULL");
+  *plan = nullptr;
+  pkv_plan* p = new (std::nothrow) pkv_plan();
+  if (p == nullptr) return fail(PKV_ERR_INVALID_ARG, "out of host memory");
+  pkv_status s = make_plan(kv_indptr_host, batch, num_qo_heads, num_kv_heads, head_dim,
+                           page_size, num_cus, allow_split, chunk_tokens, p);
+  if (s != PKV_OK) {
+    delete p;
+    return s;
+  }
+  if (workspace != nullptr) {
+    if (workspace_bytes < p->ws_bytes) {
+      const size_t need = p->ws_bytes;
+      delete p;
+      return fail(PKV_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, plan needs %zu",
+                  workspace_bytes, need);
+    }
+    if (!aligned16(workspace)) {
+      delete p;
+      return fail(PKV_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    }
+    if (!p->tables.empty()) {
+      hipError_t e = hipMemcpyAsync(workspace, p->tables.data(), p->tables.size() * sizeof(int32_t),
+                                    hipMemcpyHostToDevice, static_cast<hipStream_t>(stream));
+      if (e != hipSuccess) {
+        delete p;
+        return fail(PKV_ERR_HIP, "uploading the plan tables: %s", hipGetErrorString(e));
+      }
+    }
+    p->workspace = workspace;
+  }
+  *plan = p;
+  return ok();
+}
+
+void pkv_plan_destroy(pkv_plan* plan) { delete plan; }
+
+pkv_status pkv_plan_export(const pkv_plan* plan, int32_t* dst, size_t n_int32, size_t* needed) {
+  if (plan == nullptr) return fail(PKV_ERR_INVALID_ARG, "plan is NULL");
+  const size_t count = 4 + plan->tables.size();
+  if (needed != nullptr) *needed = count;
+  if (dst == nullptr) return ok();
+  if (n_int32 < count)
+    return fail(PKV_ERR_INVALID_ARG, "export needs %zu int32 values, got %zu", count, n_int32);
+  dst[0] = plan->part.chunk;
+  dst[1] = static_cast<int32_t>(plan->part.items.size());
+  dst[2] = static_cast<int32_t>(plan->part.merges.size());
+  dst[3] = plan->part.n_slots;
+  if (!plan->tables.empty()) std::memcpy(dst + 4, plan->tables.data(), plan->tables.size() * 4);
+  return ok();
+}
+
+pkv_status pkv_run(const pkv_plan* plan, const void* q, int32_t q_batch, int32_t q_heads,
+                   int32_t q_dim, const void* k_pool, const void* v_pool, int64_t num_pages,
+                   int32_t page_size, int32_t pool_kv_heads, int32_t pool_dim,
+                   const int32_t* kv_indptr, int64_t indptr_len, const int32_t* kv_indices,
+                   int64_t num_indices, float sm_scale, void* workspace, size_t workspace_bytes,
+                   void* out, float* lse, void* stream) {
+  if (plan == nullptr) return fail(PKV_ERR_INVALID_ARG, "plan is NULL");
+  pkv_status s = check_gqa_shape(q_heads, pool_kv_heads, q_dim, page_size);
+  if (s != PKV_OK) return s;
+  if (pool_dim != q_dim)
+    return fail(PKV_ERR_INVALID_ARG, "pool head_dim %d differs from q head_dim %d", pool_dim, q_dim);
+  if (q_batch != plan->batch || q_heads != plan->num_qo_heads || pool_kv_heads != plan->num_kv_heads ||
+      q_dim != plan->head_dim || page_size != plan->page_size)
+    return fail(PKV_ERR_PLAN_MISMATCH,
+                "call shape (B=%d, Hq=%d, Hkv=%d, D=%d, ps=%d) differs from the plan's "
+                "(B=%d, Hq=%d, Hkv=%d, D=%d, ps=%d)",
+                q_batch, q_heads, pool_kv_heads, q_dim, page_size, plan->batch,
+                plan->num_qo_heads, plan->num_kv_heads, plan->head_dim, plan->page_size);
+  if (indptr_len != static_cast<int64_t>(plan->batch) + 1)
+    return fail(PKV_ERR_INVALID_ARG, "kv_indptr has %lld entries, expected batch + 1 = %d",
+                static_cast<long long>(indptr_len), plan->batch + 1);
+  if (num_indices != plan->part.total_tokens)
+    return fail(PKV_ERR_INVALID_ARG, "kv_indices has %lld entries but kv_indptr[B] = %lld",
+                static_cast<long long>(num_indices), static_cast<long long>(plan->part.total_tokens));
+  if (num_pages < 0) return fail(PKV_ERR_INVALID_ARG, "num_pages must be >= 0");
+  if (num_indices > 0 && num_pages == 0)
+    return fail(PKV_ERR_INVALID_ARG, "kv_indices is non-empty but the pool has no pages");
+  if (!std::isfinite(sm_scale)) return fail(PKV_ERR_INVALID_ARG, "sm_scale must be finite");
+  if (plan->batch > 0) {
+    if (q == nullptr || out == nullptr || lse == nullptr || kv_indptr == nullptr)
+      return fail(PKV_ERR_INVALID_ARG, "q, out, lse and kv_indptr must be non-NULL");
+    if (num_indices > 0 && (k_pool == nullptr || v_pool == nullptr || kv_indices == nullptr))
+      return fail(PKV_ERR_INVALID_ARG, "k_pool, v_pool and kv_indices must be non-NULL");
+    if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
+      return fail(PKV_ERR_INVALID_ARG, "q, k_pool, v_pool and out must be 16-byte aligned");
+  }
+  if (plan->workspace == nullptr)
+    return fail(PKV_ERR_PLAN_MISMATCH, "host-only plan (created without a workspace)");
+  if (workspace != plan->workspace)
+    return fail(PKV_ERR_PLAN_MISMATCH, "workspace differs from the one the plan was uploaded to");
+  if (workspace_bytes < plan->ws_bytes)
+    return fail(PKV_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, plan needs %zu",
+                workspace_bytes, plan->ws_bytes);
+  if (plan->part.items.empty()) return ok();
+
+  char* ws = static_cast<char*>(workspace);
+  const float log2e = 1.4426950408889634f;
+  hipError_t e = pkv::launch_decode_partial(
+      reinterpret_cast<const int32_t*>(ws + plan->off_items),
+      static_cast<int32_t>(plan->part.items.size()), static_cast<const uint16_t*>(q),
+      static_cast<const uint16_t*>(k_pool), static_cast<const uint16_t*>(v_pool), kv_indptr,
+      kv_indices, sm_scale * log2e, static_cast<uint16_t*>(out), lse,
+      reinterpret_cast<float*>(ws + plan->off_part_o), reinterpret_cast<float*>(ws + plan->off_part_lse),
+      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+pkv_status pkv_merge(const pkv_plan* plan, void* workspace, size_t workspace_bytes, void* out,
+                     float* lse, void* stream) {
+  if (plan == nullptr) return fail(PKV_ERR_INVALID_ARG, "plan is NULL");
+  if (plan->part.merges.empty()) return ok();
+  if (out == nullptr || lse == nullptr) return fail(PKV_ERR_INVALID_ARG, "out and lse must be non-NULL");
+  if (!aligned16(out)) return fail(PKV_ERR_INVALID_ARG, "out must be 16-byte aligned");
+  if (plan->workspace == nullptr || workspace != plan->workspace)
+    return fail(PKV_ERR_PLAN_MISMATCH, "workspace differs from the one the plan was uploaded to");
+  if (workspace_bytes < plan->ws_bytes)
+    return fail(PKV_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, plan needs %zu",
+                workspace_bytes, plan->ws_bytes);
+  char* ws = static_cast<char*>(workspace);
+  hipError_t e = pkv::launch_merge(reinterpret_cast<const int32_t*>(ws + plan->off_merges),
+                                   static_cast<int32_t>(plan->part.merges.size()),
+                                   reinterpret_cast<const float*>(ws + plan->off_part_o),
+                                   reinterpret_cast<const float*>(ws + plan->off_part_lse),
+                                   static_cast<uint16_t*>(out), lse, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+pkv_status pkv_gather_mla_workspace_size(int32_t batch, int32_t num_qo_heads, int32_t d_qk,
+                                         int32_t d_v, int32_t topk, size_t* bytes) {
+  if (bytes == nullptr) return fail(PKV_ERR_INVALID_ARG, "bytes is NULL");
+  std::string err;
+  size_t need = 0;
+  const int code = pkv::mla_workspace_bytes(batch, num_qo_heads, d_qk, d_v, topk, &need, &err);
+  if (code != 0) return fail(static_cast<pkv_status>(code), "%s", err.c_str());
+  *bytes = need;
+  return ok();
+}
+
+pkv_status pkv_gather_mla(const void* q, const void* kv_pool, int64_t pool_tokens,
+                          const int32_t* indices, int32_t topk, int32_t batch,
+                          int32_t num_qo_heads, int32_t d_qk, int32_t d_v, float sm_scale,
+                          void* workspace, size_t workspace_bytes, void* out, float* lse,
+                          void* stream) {
+  std::string err;
+  size_t need = 0;
+  int code = pkv::mla_workspace_bytes(batch, num_qo_heads, d_qk, d_v, topk, &need, &err);
+  if (code != 0) return fail(static_cast<pkv_status>(code), "%s", err.c_str());
+  if (pool_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "pool_tokens must be >= 0");
+  if (!std::isfinite(sm_scale)) return fail(PKV_ERR_INVALID_ARG, "sm_scale must be finite");
+  if (batch == 0) return ok();
+  if (q == nullptr || indices == nullptr || out == nullptr || lse == nullptr)
+    return fail(PKV_ERR_INVALID_ARG, "q, indices, out and lse must be non-NULL");
+  if (pool_tokens > 0 && kv_pool == nullptr) return fail(PKV_ERR_INVALID_ARG, "kv_pool is NULL");
+  if (!aligned16(q) || !aligned16(kv_pool) || !aligned16(out) || !aligned16(workspace))
+    return fail(PKV_ERR_INVALID_ARG, "q, kv_pool, out and workspace must be 16-byte aligned");
+  if (need > 0 && workspace == nullptr) return fail(PKV_ERR_INVALID_ARG, "workspace is NULL");
+  if (workspace_bytes < need)
+    return fail(PKV_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, gather needs %zu",
+                workspace_bytes, need);
+  hipError_t e = pkv::launch_gather_mla(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv_pool), pool_tokens, indices,
+      topk, batch, num_qo_heads, sm_scale, workspace, static_cast<uint16_t*>(out), lse,
+      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "gather launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,322 @@
+// Paged GQA decode for gfx950 (MI355X): Hq = 32, Hkv = 4, head_dim = 128,
+// page size 1, bf16 q/K/V, fp32 accumulation, base-2 LSE.
+//
+// What is computed follows kernelindex.com, "flashinfer gemini-2.5-pro /
+// triton h7ykt0" (gqa_paged_decode_h32_kv4_d128_ps1, steps 4-9): gather each
+// token's K and V row through the CSR page list, scaled q.k scores, online
+// softmax, P.V, then out = acc / l and lse = log2 of the exp-sum. The split into
+// chunks with normalised fp32 partials and an LSE merge follows the vLLM fork
+// qsa.py (_qsa_sparse_paged_gqa_splitk_kernel, _qsa_merge_splitk_kernel).
+//
+// Design (gfx950, wave64):
+// * One workgroup per work item (b, token range); wave w handles KV head w and
+//   its 8 query heads. A wave walks its range in tiles of 32 tokens.
+// * Both contractions run on v_mfma_f32_16x16x32_bf16, the 8 query heads
+//   padded to 16 MFMA columns:
+//     S^T[tok, h] = K[tok, :] . Q[h, :]        A = K rows as loaded, B = Q^T
+//     O^T[d, h]  += V^T[d, tok] . P^T[tok, h]  A = V^T read back from LDS, B = P^T
+//   The S^T accumulator leaves lane (r, c) = (lane % 16, lane / 16) with head r
+//   and tokens 16*mb + 4c + i, which is exactly the token set the P^T operand
+//   of lane (r, c) needs, so P never crosses lanes. The MFMA only needs A and B
+//   to agree on the order of the contracted index, so neither K nor P is
+//   shuffled.
+// * K/V rows are gathered straight into registers: lane (r, c) reads bytes
+//   [64x + 16c, +16) of the 256-byte (page, KV head) row of token 16*mb + r,
+//   so one load instruction covers 64 contiguous bytes of 16 rows.
+// * V is written to LDS row-major (272-byte padded rows, conflict-free) and
+//   read back transposed (8 tokens of one dim per lane) as the A operand.
+// * Loads are software-pipelined one tile ahead (page ids two tiles ahead);
+//   out-of-range tokens of the last tile re-read the item's last page, which
+//   keeps every load unconditional, and get score -inf, i.e. weight exactly 0.
+// * Scores are scaled by sm_scale*log2(e) in fp32 and exponentiated with
+//   exp2; the running max is reduced across the 4 lane rows with shuffles,
+//   the running sum is kept per lane and reduced once at the end.
+#include <hip/hip_runtime.h>
+
+#include "kernels.h"
+
+namespace pkv {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kGroup = kHq / kHkv;      // query heads per KV head
+constexpr int kTileTok = 32;            // tokens per wave per step
+constexpr int kRowU16 = kHeadDim + 8;   // LDS row of one token's V: 256 B + 16 B pad
+constexpr int kWaveLdsU16 = kTileTok * kRowU16;
+constexpr int kThreads = 64 * kHkv;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+struct Tile {
+  u32x4 k[2][4];  // [mb][x]: bytes [64x + 16c, +16) of the K row of token 16*mb + r
+  u32x4 v[2][4];
+};
+
+struct Softmax {
+  f32x4 acc[8];   // O^T blocks: acc[db][i] = O[head r][16*db + 4c + i]
+  float m;        // running max of the log2-domain scores (equal on the 4 lane rows)
+  float l;        // this lane's share of the running exp-sum
+};
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+
+__device__ __forceinline__ uint16_t bf16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+__device__ __forceinline__ void load_tile(Tile& t, const uint16_t* __restrict__ k_pool,
+                                          const uint16_t* __restrict__ v_pool, int32_t page0,
+                                          int32_t page1, int g, int c) {
+  const int64_t r0 = (static_cast<int64_t>(page0) * kHkv + g) * kHeadDim + c * 8;
+  const int64_t r1 = (static_cast<int64_t>(page1) * kHkv + g) * kHeadDim + c * 8;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    t.k[0][x] = *reinterpret_cast<const u32x4*>(k_pool + r0 + x * 32);
+    t.k[1][x] = *reinterpret_cast<const u32x4*>(k_pool + r1 + x * 32);
+  }
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    t.v[0][x] = *reinterpret_cast<const u32x4*>(v_pool + r0 + x * 32);
+    t.v[1][x] = *reinterpret_cast<const u32x4*>(v_pool + r1 + x * 32);
+  }
+}
+
+// Orders this wave's LDS writes before its later LDS reads (and the reverse).
+__device__ __forceinline__ void lds_wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ void compute_tile(const Tile& t, int t0, int n, const u32x4 (&qf)[4],
+                                             float scale_log2, int r, int c, uint16_t* lw,
+                                             Softmax& st) {
+  // Scores of the 32 tokens against the (padded) 16 heads.
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f};
+  f32x4 s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(t.k[0][x]), as_bf16x8(qf[x]), s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(t.k[1][x]), as_bf16x8(qf[x]), s1, 0, 0, 0);
+  }
+  // p[4*mb + i] belongs to token t0 + 16*mb + 4c + i.
+  float p[8];
+  float mx = kNegInf;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tok = t0 + 4 * c + i;
+    p[i] = (tok < n) ? s0[i] * scale_log2 : kNegInf;
+    p[4 + i] = (tok + 16 < n) ? s1[i] * scale_log2 : kNegInf;
+    mx = fmaxf(mx, fmaxf(p[i], p[4 + i]));
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(st.m, mx);   // finite: every tile holds a valid token
+  const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+  float psum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    p[j] = __builtin_amdgcn_exp2f(p[j] - m_new);
+    psum += p[j];
+  }
+  st.l = st.l * alpha + psum;
+  st.m = m_new;
+#pragma unroll
+  for (int db = 0; db < 8; ++db) st.acc[db] *= alpha;
+
+  // V rows to LDS (row-major, padded rows).
+  lds_wave_sync();
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      *reinterpret_cast<u32x4*>(lw + (16 * mb + r) * kRowU16 + 32 * x + 8 * c) = t.v[mb][x];
+    }
+  }
+  lds_wave_sync();
+
+  bf16x8 pb;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) pb[j] = static_cast<__bf16>(p[j]);
+
+  // A operand of block db: V[token 16*(j/4) + 4c + j%4][16*db + r], j = 0..7.
+#pragma unroll
+  for (int db = 0; db < 8; ++db) {
+    u16x8 e;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      e[j] = lw[(16 * (j >> 2) + 4 * c + (j & 3)) * kRowU16 + 16 * db + r];
+    }
+    st.acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, e), pb,
+                                                         st.acc[db], 0, 0, 0);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void decode_partial_kernel(
+    const int32_t* __restrict__ items, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ k_pool, const uint16_t* __restrict__ v_pool,
+    const int32_t* __restrict__ kv_indptr, const int32_t* __restrict__ kv_indices,
+    float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
+    float* __restrict__ part_o, float* __restrict__ part_lse) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kHkv * kWaveLdsU16];
+  const int lane = threadIdx.x & 63;
+  const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // KV head of this wave
+  const int r = lane & 15;
+  const int c = lane >> 4;
+  const int32_t* it = items + 4 * blockIdx.x;
+  const int b = it[0];
+  const int lo = it[1];
+  const int n = it[2] - lo;
+  const int slot = it[3];
+  const int head = g * kGroup + r;   // a real query head only for r < kGroup
+
+  if (n == 0) {   // empty sequence: out = 0, lse = -inf
+    if (r < kGroup) {
+      uint16_t* o = out + (static_cast<int64_t>(b) * kHq + head) * kHeadDim + 4 * c;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) *reinterpret_cast<u32x2*>(o + 16 * db) = u32x2{0u, 0u};
+      if (c == 0) lse[b * kHq + head] = kNegInf;
+    }
+    return;
+  }
+
+  const int32_t* ids = kv_indices + kv_indptr[b] + lo;
+  const int last = n - 1;
+
+  // Q as the B operand: lane (r, c) holds q[head r][32x + 8c, +8) for k-step x.
+  u32x4 qf[4];
+  if (r < kGroup) {
+    const uint16_t* qh = q + (static_cast<int64_t>(b) * kHq + head) * kHeadDim + 8 * c;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) qf[x] = *reinterpret_cast<const u32x4*>(qh + 32 * x);
+  } else {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) qf[x] = u32x4{0u, 0u, 0u, 0u};
+  }
+
+  Softmax st;
+#pragma unroll
+  for (int db = 0; db < 8; ++db) st.acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m = kNegInf;
+  st.l = 0.f;
+  uint16_t* lw = lds + g * kWaveLdsU16;
+
+  // Pipeline: ids two tiles ahead, K/V one tile ahead.
+  int32_t pa0 = ids[min(r, last)];
+  int32_t pa1 = ids[min(16 + r, last)];
+  int32_t pb0 = ids[min(32 + r, last)];
+  int32_t pb1 = ids[min(48 + r, last)];
+  Tile ta, tb;
+  load_tile(ta, k_pool, v_pool, pa0, pa1, g, c);
+  for (int t0 = 0;;) {
+    pa0 = ids[min(t0 + 64 + r, last)];
+    pa1 = ids[min(t0 + 80 + r, last)];
+    load_tile(tb, k_pool, v_pool, pb0, pb1, g, c);
+    compute_tile(ta, t0, n, qf, scale_log2, r, c, lw, st);
+    t0 += kTileTok;
+    if (t0 >= n) break;
+    pb0 = ids[min(t0 + 64 + r, last)];
+    pb1 = ids[min(t0 + 80 + r, last)];
+    load_tile(ta, k_pool, v_pool, pa0, pa1, g, c);
+    compute_tile(tb, t0, n, qf, scale_log2, r, c, lw, st);
+    t0 += kTileTok;
+    if (t0 >= n) break;
+  }
+
+  float l_tot = st.l + __shfl_xor(st.l, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  const float inv = 1.0f / l_tot;
+  const float lse2 = st.m + __log2f(l_tot);
+  if (r < kGroup) {
+    if (slot < 0) {
+      uint16_t* o = out + (static_cast<int64_t>(b) * kHq + head) * kHeadDim + 4 * c;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const f32x4 v = st.acc[db] * inv;
+        const u32x2 w = {static_cast<uint32_t>(bf16_bits(v[0])) |
+                             (static_cast<uint32_t>(bf16_bits(v[1])) << 16),
+                         static_cast<uint32_t>(bf16_bits(v[2])) |
+                             (static_cast<uint32_t>(bf16_bits(v[3])) << 16)};
+        *reinterpret_cast<u32x2*>(o + 16 * db) = w;
+      }
+      if (c == 0) lse[b * kHq + head] = lse2;
+    } else {
+      float* o = part_o + (static_cast<int64_t>(slot) * kHq + head) * kHeadDim + 4 * c;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(o + 16 * db) = st.acc[db] * inv;
+      if (c == 0) part_lse[static_cast<int64_t>(slot) * kHq + head] = lse2;
+    }
+  }
+}
+
+// One workgroup per split sequence: thread t merges head t/8, dims 16*(t%8) .. +16.
+__global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ merges,
+                                                    const float* __restrict__ part_o,
+                                                    const float* __restrict__ part_lse,
+                                                    uint16_t* __restrict__ out,
+                                                    float* __restrict__ lse) {
+  const int32_t* m = merges + 4 * blockIdx.x;
+  const int b = m[0];
+  const int first = m[1];
+  const int k = m[2];
+  const int h = threadIdx.x >> 3;
+  const int d0 = (threadIdx.x & 7) * 16;
+
+  float top = kNegInf;
+  for (int i = 0; i < k; ++i) top = fmaxf(top, part_lse[static_cast<int64_t>(first + i) * kHq + h]);
+
+  f32x4 acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  float den = 0.f;
+  if (top != kNegInf) {
+    for (int i = 0; i < k; ++i) {
+      const int64_t s = static_cast<int64_t>(first + i) * kHq + h;
+      const float li = part_lse[s];
+      const float w = (li == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(li - top);
+      den += w;
+      const f32x4* src = reinterpret_cast<const f32x4*>(part_o + s * kHeadDim + d0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] += w * src[j];
+    }
+  }
+  const float inv = (den > 0.f) ? 1.0f / den : 0.f;
+  uint16_t* o = out + (static_cast<int64_t>(b) * kHq + h) * kHeadDim + d0;
+  u32x4 w0, w1;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t lo16 = bf16_bits(acc[j >> 1][(2 * j) & 3] * inv);
+    const uint32_t hi16 = bf16_bits(acc[j >> 1][(2 * j + 1) & 3] * inv);
+    const uint32_t word = lo16 | (hi16 << 16);
+    if (j < 4) w0[j] = word; else w1[j - 4] = word;
+  }
+  reinterpret_cast<u32x4*>(o)[0] = w0;
+  reinterpret_cast<u32x4*>(o)[1] = w1;
+  if ((threadIdx.x & 7) == 0) lse[b * kHq + h] = (den > 0.f) ? top + __log2f(den) : kNegInf;
+}
+
+}  // namespace
+
+hipError_t launch_decode_partial(const int32_t* items, int32_t n_items, const uint16_t* q,
+                                 const uint16_t* k_pool, const uint16_t* v_pool,
+                                 const int32_t* kv_indptr, const int32_t* kv_indices,
+                                 float sm_scale_log2, uint16_t* out, float* lse,
+                                 float* part_o, float* part_lse, hipStream_t stream) {
+  if (n_items <= 0) return hipSuccess;
+  hipLaunchKernelGGL(decode_partial_kernel, dim3(n_items), dim3(kThreads), 0, stream, items, q,
+                     k_pool, v_pool, kv_indptr, kv_indices, sm_scale_log2, out, lse, part_o,
+                     part_lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const int32_t* merges, int32_t n_merges, const float* part_o,
+                        const float* part_lse, uint16_t* out, float* lse, hipStream_t stream) {
+  if (n_merges <= 0) return hipSuccess;
+  hipLaunchKernelGGL(merge_kernel, dim3(n_merges), dim3(256), 0, stream, merges, part_o, part_lse,
+                     out, lse);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -1,0 +1,31 @@
+// Kernel launchers of the paged-decode library (implemented in decode.hip and
+// mla.hip). All pointers are device pointers; launches are asynchronous on
+// `stream` and return the launch's hipError_t.
+#ifndef PKV_KERNELS_H_
+#define PKV_KERNELS_H_
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+
+namespace pkv {
+
+// Paged GQA decode, Hq = 32, Hkv = 4, D = 128, page size 1.
+constexpr int kHq = 32;
+constexpr int kHkv = 4;
+constexpr int kHeadDim = 128;
+
+// One workgroup per work item (b, tok_begin, tok_end, slot) of `items`.
+hipError_t launch_decode_partial(const int32_t* items, int32_t n_items, const uint16_t* q,
+                                 const uint16_t* k_pool, const uint16_t* v_pool,
+                                 const int32_t* kv_indptr, const int32_t* kv_indices,
+                                 float sm_scale_log2, uint16_t* out, float* lse,
+                                 float* part_o, float* part_lse, hipStream_t stream);
+
+// One workgroup per merge record (b, first_slot, n_chunks, 0).
+hipError_t launch_merge(const int32_t* merges, int32_t n_merges, const float* part_o,
+                        const float* part_lse, uint16_t* out, float* lse, hipStream_t stream);
+
+}  // namespace pkv
+
+#endif  // PKV_KERNELS_H_

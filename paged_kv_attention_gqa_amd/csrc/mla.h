@@ -1,0 +1,30 @@
+// Index-gather latent-attention decode (bf16 latent rows of 576 dims whose
+// first 512 dims are the values). Implemented in mla.hip.
+#ifndef PKV_MLA_H_
+#define PKV_MLA_H_
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+namespace pkv {
+
+constexpr int kMlaDqk = 576;
+constexpr int kMlaDv = 512;
+constexpr int kMlaMaxHeads = 128;
+
+// Checks the gather shape; returns 0 and the workspace size, or a pkv_status
+// code with a message.
+int mla_workspace_bytes(int32_t batch, int32_t num_qo_heads, int32_t d_qk, int32_t d_v,
+                        int32_t topk, size_t* bytes, std::string* err);
+
+hipError_t launch_gather_mla(const uint16_t* q, const uint16_t* kv_pool, int64_t pool_tokens,
+                             const int32_t* indices, int32_t topk, int32_t batch,
+                             int32_t num_qo_heads, float sm_scale, void* workspace,
+                             uint16_t* out, float* lse, hipStream_t stream);
+
+}  // namespace pkv
+
+#endif  // PKV_MLA_H_

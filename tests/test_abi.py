@@ -1,0 +1,216 @@
+"""The C ABI on the host: every declared symbol is exported, every argument
+check returns its status before any HIP call, and the exported plan equals the
+independent Python statement of the partition rule integer for integer.
+
+No test here launches a kernel; the fake device pointers passed below are never
+dereferenced because each call is rejected by a host-side check first.
+"""
+
+import ctypes
+import pathlib
+import re
+
+import numpy as np
+import pytest
+
+import paged_kv_attention_gqa_amd as pkv
+from inputs import lognormal_lengths
+from inputs.configs import EDGE_LENGTHS
+from oracle import plan_ref
+
+HEADER = pathlib.Path(__file__).resolve().parents[1] / "include" / "pkv.h"
+FAKE = 0x10000   # 16-byte aligned, never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    try:
+        return pkv.lib()
+    except RuntimeError as e:
+        pytest.fail(str(e))
+
+
+def declared_symbols():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_symbols()
+    assert len(names) == 10
+    for name in names:
+        assert hasattr(lib, name), name
+        assert name in pkv.SIGNATURES, name
+
+
+def test_status_strings(lib):
+    for code in range(6):
+        assert pkv.pkv_status_string(code)
+    assert pkv.pkv_status_string(99) == "unknown status"
+
+
+def _indptr(lengths):
+    return np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+
+
+def _ws(ind, **kw):
+    out = ctypes.c_size_t(0)
+    args = dict(hq=32, hkv=4, d=128, ps=1, cus=256, split=1, chunk=0)
+    args.update(kw)
+    st = pkv.lib().pkv_workspace_size(ind.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                      len(ind) - 1, args["hq"], args["hkv"], args["d"],
+                                      args["ps"], args["cus"], args["split"], args["chunk"],
+                                      ctypes.byref(out))
+    return st, out.value
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hq=16), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(hkv=8), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(d=64), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(ps=16), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(hq=30), pkv.PKV_ERR_INVALID_ARG),       # not a multiple of Hkv
+    (dict(hq=0), pkv.PKV_ERR_INVALID_ARG),
+    (dict(chunk=-1), pkv.PKV_ERR_INVALID_ARG),
+    (dict(cus=-3), pkv.PKV_ERR_INVALID_ARG),
+])
+def test_shape_checks(lib, kw, status):
+    st, _ = _ws(_indptr([3, 4]), **kw)
+    assert st == status
+    assert pkv.pkv_last_error()
+
+
+def test_indptr_checks(lib):
+    assert _ws(np.array([1, 5], np.int32))[0] == pkv.PKV_ERR_INVALID_ARG
+    assert _ws(np.array([0, 5, 4], np.int32))[0] == pkv.PKV_ERR_INVALID_ARG
+    out = ctypes.c_size_t(0)
+    assert lib.pkv_workspace_size(None, 2, 32, 4, 128, 1, 256, 1, 0, ctypes.byref(out)) == \
+        pkv.PKV_ERR_INVALID_ARG
+    st, n = _ws(_indptr([]))
+    assert st == pkv.PKV_OK
+
+
+def test_workspace_size_formula(lib):
+    ind = _indptr([1000, 10, 0, 5000])
+    st, n = _ws(ind, chunk=256)
+    assert st == pkv.PKV_OK
+    c_len, items, merges, slots = plan_ref.make_plan(ind, 256, True, 256)
+    al = lambda x: -(-x // 256) * 256
+    tables = 16 * (len(items) + len(merges))
+    part_o = al(tables)
+    part_lse = al(part_o + slots * 32 * 128 * 4)
+    assert n == al(part_lse + slots * 32 * 4)
+
+
+def _host_plan(ind, cus, split, chunk):
+    plan = pkv.pkv_plan_create(ind, num_cus=cus, allow_split=split, chunk_tokens=chunk)
+    return pkv.pkv_plan_export(plan)
+
+
+PLAN_CASES = [
+    ("tiny", _indptr([17, 64])),
+    ("edge", _indptr(list(EDGE_LENGTHS))),
+    ("gqa", _indptr(np.random.default_rng(2).integers(512, 4096, size=64, endpoint=True))),
+    ("throughput", _indptr(lognormal_lengths(np.random.default_rng(4), 256))),
+    ("empty_batch", _indptr([])),
+    ("all_empty", _indptr([0, 0, 0])),
+]
+
+
+@pytest.mark.parametrize("name,ind", PLAN_CASES, ids=[c[0] for c in PLAN_CASES])
+@pytest.mark.parametrize("cus,split,chunk", [(256, True, 0), (256, False, 0), (80, True, 0),
+                                             (256, True, 64), (1, True, 0), (304, True, 1000)])
+def test_plan_export_matches_rule(lib, name, ind, cus, split, chunk):
+    assert _host_plan(ind, cus, split, chunk) == plan_ref.export(ind, cus, split, chunk)
+
+
+@pytest.mark.parametrize("seed", range(25))
+def test_plan_export_random(lib, seed):
+    rng = np.random.default_rng(1000 + seed)
+    batch = int(rng.integers(0, 400))
+    lengths = rng.integers(0, 40000, size=batch) * (rng.random(batch) < 0.8)
+    ind = _indptr(lengths)
+    cus = int(rng.choice([1, 7, 256, 304]))
+    chunk = int(rng.choice([0, 0, 0, 1, 33, 512]))
+    split = bool(rng.random() < 0.9)
+    assert _host_plan(ind, cus, split, chunk) == plan_ref.export(ind, cus, split, chunk)
+
+
+def _run_raw(plan_handle, **over):
+    a = dict(q=FAKE, qb=2, qh=32, qd=128, k=FAKE, v=FAKE, pages=128, ps=1, hkv=4, pd=128,
+             indptr=FAKE, indptr_len=3, indices=FAKE, nidx=81, scale=0.088, ws=FAKE,
+             ws_bytes=1 << 20, out=FAKE, lse=FAKE, stream=0)
+    a.update(over)
+    return pkv.lib().pkv_run(plan_handle, a["q"], a["qb"], a["qh"], a["qd"], a["k"], a["v"],
+                             a["pages"], a["ps"], a["hkv"], a["pd"], a["indptr"],
+                             a["indptr_len"], a["indices"], a["nidx"], a["scale"], a["ws"],
+                             a["ws_bytes"], a["out"], a["lse"], a["stream"])
+
+
+def test_run_checks_before_any_hip_call(lib):
+    ind = _indptr([17, 64])
+    host_plan = pkv.pkv_plan_create(ind, num_cus=256)
+    h = host_plan.handle
+    E = pkv
+    assert _run_raw(None) == E.PKV_ERR_INVALID_ARG
+    assert _run_raw(h, qh=16) == E.PKV_ERR_UNSUPPORTED
+    assert _run_raw(h, qd=64, pd=64) == E.PKV_ERR_UNSUPPORTED
+    assert _run_raw(h, ps=2) == E.PKV_ERR_UNSUPPORTED
+    assert _run_raw(h, pd=64) == E.PKV_ERR_INVALID_ARG
+    assert _run_raw(h, qb=3) == E.PKV_ERR_PLAN_MISMATCH
+    assert _run_raw(h, indptr_len=4) == E.PKV_ERR_INVALID_ARG
+    assert _run_raw(h, nidx=80) == E.PKV_ERR_INVALID_ARG
+    assert _run_raw(h, scale=float("nan")) == E.PKV_ERR_INVALID_ARG
+    assert _run_raw(h, scale=float("inf")) == E.PKV_ERR_INVALID_ARG
+    assert _run_raw(h, q=0) == E.PKV_ERR_INVALID_ARG
+    assert _run_raw(h, k=0) == E.PKV_ERR_INVALID_ARG
+    assert _run_raw(h, q=FAKE + 2) == E.PKV_ERR_INVALID_ARG      # misaligned
+    assert _run_raw(h, pages=0) == E.PKV_ERR_INVALID_ARG
+    # a host-only plan can be exported but never run
+    assert _run_raw(h) == E.PKV_ERR_PLAN_MISMATCH
+    assert pkv.lib().pkv_merge(None, FAKE, 1, FAKE, FAKE, 0) == E.PKV_ERR_INVALID_ARG
+
+
+def test_plan_create_checks(lib):
+    ind = _indptr([17, 64])
+    handle = ctypes.c_void_p(0)
+    I32P = ctypes.POINTER(ctypes.c_int32)
+    st = lib.pkv_plan_create(ind.ctypes.data_as(I32P), 2, 32, 4, 128, 1, 256, 1, 0, FAKE, 16, 0,
+                             ctypes.byref(handle))
+    assert st == pkv.PKV_ERR_WORKSPACE_TOO_SMALL and not handle.value
+    assert lib.pkv_plan_create(ind.ctypes.data_as(I32P), 2, 32, 4, 128, 1, 256, 1, 0, None, 0, 0,
+                               None) == pkv.PKV_ERR_INVALID_ARG
+    assert lib.pkv_plan_create(ind.ctypes.data_as(I32P), 2, 32, 4, 64, 1, 256, 1, 0, None, 0, 0,
+                               ctypes.byref(handle)) == pkv.PKV_ERR_UNSUPPORTED
+    with pytest.raises(ValueError):
+        pkv.pkv_plan_create(ind, head_dim=64, num_cus=256)
+
+
+def test_plan_export_small_buffer(lib):
+    plan = pkv.pkv_plan_create(_indptr([17, 64]), num_cus=256)
+    need = ctypes.c_size_t(0)
+    assert lib.pkv_plan_export(plan.handle, None, 0, ctypes.byref(need)) == pkv.PKV_OK
+    buf = (ctypes.c_int32 * (need.value - 1))()
+    assert lib.pkv_plan_export(plan.handle, buf, need.value - 1, None) == pkv.PKV_ERR_INVALID_ARG
+
+
+def test_gather_checks(lib):
+    out = ctypes.c_size_t(0)
+    assert lib.pkv_gather_mla_workspace_size(32, 128, 576, 512, 2048, ctypes.byref(out)) == pkv.PKV_OK
+    assert lib.pkv_gather_mla_workspace_size(32, 128, 512, 512, 2048, ctypes.byref(out)) == \
+        pkv.PKV_ERR_UNSUPPORTED
+    assert lib.pkv_gather_mla_workspace_size(32, 100, 576, 512, 2048, ctypes.byref(out)) == \
+        pkv.PKV_ERR_UNSUPPORTED
+    assert lib.pkv_gather_mla_workspace_size(-1, 128, 576, 512, 2048, ctypes.byref(out)) == \
+        pkv.PKV_ERR_INVALID_ARG
+    g = lambda **o: lib.pkv_gather_mla(
+        o.get("q", FAKE), o.get("kv", FAKE), o.get("T", 65536), o.get("idx", FAKE),
+        o.get("topk", 2048), o.get("B", 32), o.get("H", 128), o.get("dqk", 576), o.get("dv", 512),
+        o.get("scale", 0.04), o.get("ws", FAKE), o.get("wsb", 1 << 30), o.get("out", FAKE),
+        o.get("lse", FAKE), 0)
+    assert g(dqk=512) == pkv.PKV_ERR_UNSUPPORTED
+    assert g(scale=float("nan")) == pkv.PKV_ERR_INVALID_ARG
+    assert g(q=0) == pkv.PKV_ERR_INVALID_ARG
+    assert g(T=-1) == pkv.PKV_ERR_INVALID_ARG
+    assert g(out=FAKE + 4) == pkv.PKV_ERR_INVALID_ARG

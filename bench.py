@@ -48,15 +48,16 @@ def algorithmic_decode_bytes(w, plan_flat) -> int:
 
     Per token: 2048 B of K/V rows + 4 B page id. Per sequence: 8192 B of q and
     the 4-byte indptr entry. Per directly written sequence: 8192 B bf16 out +
-    128 B lse. Per split chunk: 16384 B fp32 partial + 128 B partial LSE. Plus
-    16 B per work item of plan table.
+    128 B lse. Per split segment: 16384 B fp32 partial + 128 B partial LSE.
+    Plus the plan tables: 4 B per worker offset and 16 B per segment.
     """
-    _, n_items, n_merges, n_slots = plan_flat[:4]
-    items = np.array(plan_flat[4:4 + 4 * n_items], dtype=np.int64).reshape(-1, 4)
-    direct = int(np.sum(items[:, 3] < 0))
+    n_workers, n_segs, n_merges, n_slots = plan_flat[:4]
+    segs = np.array(plan_flat[5 + n_workers:5 + n_workers + 4 * n_segs],
+                    dtype=np.int64).reshape(-1, 4)
+    direct = int(np.sum(segs[:, 3] < 0))
     n = w.total_tokens
     return (2052 * n + 8192 * w.batch + 4 * (w.batch + 1) + direct * (8192 + 128)
-            + n_slots * (16384 + 128) + 16 * n_items)
+            + n_slots * (16384 + 128) + 4 * (n_workers + 1) + 16 * n_segs)
 
 
 def read_traffic(kernel_src: str):
@@ -206,8 +207,8 @@ def main():
         "data": "synthetic (seeded N(0,1) bf16 q/K/V, random page permutation)",
         "config": {"workload": WORKLOAD_TEXT[args.config], "name": args.config,
                    "batch": w.batch, "total_tokens": w.total_tokens,
-                   "split": not args.no_split, "chunk_tokens": flat[0], "work_items": flat[1],
-                   "split_sequences": flat[2], "pool_replicas": reps,
+                   "split": not args.no_split, "workers": flat[0], "segments": flat[1],
+                   "merge_records": flat[2], "partial_slots": flat[3], "pool_replicas": reps,
                    "plan_host_us": round(plan_us, 1)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),

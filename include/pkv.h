@@ -63,9 +63,9 @@ typedef struct pkv_plan pkv_plan;
  * fp32 partials of split sequences). Same arguments as pkv_plan_create.
  * kv_indptr_host: host int32 [batch + 1], non-decreasing, kv_indptr_host[0] == 0.
  * num_cus: compute units to plan for; 0 queries the current HIP device.
- * allow_split: 0 keeps every sequence in one work item (no merge needed).
- * chunk_tokens: chunk length override (rounded up to 32); 0 chooses it from
- * the total token count and num_cus.
+ * allow_split: 0 gives one worker per sequence (nothing to merge).
+ * chunk_tokens: tokens per worker; 0 uses two workers per CU (fewer for a
+ * batch of under 128 tokens per worker).
  */
 pkv_status pkv_workspace_size(const int32_t* kv_indptr_host, int32_t batch,
                               int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
@@ -95,18 +95,22 @@ void pkv_plan_destroy(pkv_plan* plan);
 
 /*
  * Copy the plan's integer tables to host memory:
- * [chunk, n_items, n_merges, n_slots], then n_items records
- * (b, tok_begin, tok_end, slot) with slot -1 for a sequence written directly,
- * then n_merges records (b, first_slot, n_chunks, 0). *needed receives the
- * count of int32 values; dst may be NULL to query it. Fails with
- * PKV_ERR_INVALID_ARG when n_int32 is smaller than that count.
+ * [n_workers, n_segments, n_merges, n_slots], then n_workers + 1 offsets of
+ * each worker's first segment, then n_segments records
+ * (b, tok_begin, tok_end, slot) with token positions relative to sequence b
+ * and slot -1 for a sequence written directly, then n_merges records
+ * (b, first_slot, n_segments, 0) (n_segments 0 for an empty sequence).
+ * Worker w (one workgroup) owns an equal share of the batch's tokens taken in
+ * kv_indices order. *needed receives the count of int32 values; dst may be
+ * NULL to query it. Fails with PKV_ERR_INVALID_ARG when n_int32 is smaller
+ * than that count.
  */
 pkv_status pkv_plan_export(const pkv_plan* plan, int32_t* dst, size_t n_int32, size_t* needed);
 
 /*
- * Enqueue the partial-decode kernel for every work item of the plan. Sequences
- * in one chunk get their final out/lse; split sequences get fp32 partials in
- * the workspace, finished by pkv_merge. Shapes are passed so that they can be
+ * Enqueue the partial-decode kernel: one workgroup per worker of the plan.
+ * Sequences inside one worker get their final out/lse; split sequences get
+ * fp32 partials in the workspace, finished by pkv_merge. Shapes are passed so that they can be
  * checked against the plan: q is [q_batch, q_heads, q_dim], each pool is
  * [num_pages, page_size, pool_kv_heads, pool_dim], kv_indptr has indptr_len
  * entries and kv_indices has num_indices entries (must equal the plan's
@@ -123,10 +127,12 @@ pkv_status pkv_run(const pkv_plan* plan,
                    void* out, float* lse, void* stream);
 
 /*
- * Enqueue the LSE merge of split sequences (a no-op when the plan split
- * nothing): lse* = max_i lse_i, w_i = 2^(lse_i - lse*),
- * out = sum_i w_i o_i / sum_i w_i, lse = lse* + log2(sum_i w_i).
- * Must follow pkv_run on the same stream with the same workspace.
+ * Enqueue the LSE merge of the sequences the plan split (and the zero output
+ * of empty sequences); always call it after pkv_run, on the same stream with
+ * the same workspace. Per (sequence, head): lse* = max_i lse_i,
+ * w_i = 2^(lse_i - lse*), out = sum_i w_i o_i / sum_i w_i,
+ * lse = lse* + log2(sum_i w_i); no pieces (or all -inf) gives out = 0,
+ * lse = -inf. It enqueues nothing when there is nothing to merge.
  */
 pkv_status pkv_merge(const pkv_plan* plan, void* workspace, size_t workspace_bytes,
                      void* out, float* lse, void* stream);

@@ -5,83 +5,97 @@ this, integer for integer. It shares no code with the library.
 
 The pages fix only the ideas: a plan object captured once and reused
 ([MLA page] ``FlashMLASchedMeta`` / ``get_mla_metadata``), splitting one row's
-keys into contiguous tiles with no empty split and merging the partials by LSE
-([QSA page] ``qsa_sparse_paged_attention`` and its split-K kernel). The exact
-rule is this library's own and is stated here once:
+keys into contiguous pieces with no empty piece and merging the partials by
+LSE ([QSA page] ``qsa_sparse_paged_attention`` and its split-K kernel). The
+exact rule is this library's own and is stated here once:
 
-* ``N = kv_indptr[B]``. The chunk length ``C`` is ``chunk_tokens`` rounded up to
-  a multiple of ``TILE`` when given; otherwise
-  ``max(MIN_CHUNK, roundup(ceil(N / (num_cus * ITEMS_PER_CU)), TILE))``.
-  Without splitting, ``C`` is unbounded.
-* A sequence with ``n = 0`` tokens gets one item ``(b, 0, 0, -1)`` that writes
-  zeros and -inf. A sequence with ``0 < n <= C`` gets one item
-  ``(b, 0, n, -1)`` that writes the final output directly.
-* A longer sequence gets ``k = ceil(n / C)`` chunks of equal tile-rounded
-  length ``c = roundup(ceil(n / k), TILE)`` (then ``k = ceil(n / c)``, so no
-  chunk is empty): items ``(b, j*c, min((j+1)*c, n), slot0 + j)``, and one
-  merge record ``(b, slot0, k, 0)``. Partial slots are numbered in sequence
-  order.
-* Items are ordered by token count, longest first; equal counts keep the order
-  in which they were made (sequence order, then chunk order).
+* The batch's ``N = kv_indptr[B]`` tokens, in ``kv_indices`` order, go to
+  ``W`` workers; worker ``w`` owns positions ``[w*N//W, (w+1)*N//W)``.
+  ``W = ceil(N / chunk_tokens)`` when ``chunk_tokens > 0``, else
+  ``min(num_cus * WORKERS_PER_CU, ceil(N / MIN_WORKER_TOKENS))``; ``W = 0``
+  when ``N = 0``.
+* Each non-empty sequence becomes one segment per worker it overlaps:
+  ``(b, lo, hi, slot)`` with ``lo, hi`` relative to the sequence. A sequence
+  inside one worker has ``slot = -1`` (written directly); a sequence cut into
+  ``k`` segments gets slots ``s0 .. s0+k-1`` in token order and a merge record
+  ``(b, s0, k, 0)``; slots are numbered in sequence order.
+* An empty sequence has no segment and a merge record ``(b, 0, 0, 0)``.
+  Merge records are in sequence order.
+* Without splitting, every non-empty sequence is its own worker with one
+  segment ``(b, 0, n, -1)``, workers ordered longest first (ties by ``b``).
 
-The export layout is ``[C, n_items, n_merges, n_slots]`` then the items
-(4 int32 each) then the merge records (4 int32 each).
+Export layout: ``[W, n_segments, n_merges, n_slots]``, then ``W + 1`` worker
+offsets into the segment list, then the segments (4 int32 each), then the
+merge records (4 int32 each).
 """
 
 from __future__ import annotations
 
-TILE = 32
-MIN_CHUNK = 256
-ITEMS_PER_CU = 2
-NO_SPLIT_CHUNK = 2**31 - 1
+import bisect
+
+WORKERS_PER_CU = 2
+MIN_WORKER_TOKENS = 128
 
 
 def _cdiv(a: int, b: int) -> int:
     return -(-a // b)
 
 
-def _roundup(a: int, m: int) -> int:
-    return _cdiv(a, m) * m
-
-
-def chunk_length(total_tokens: int, num_cus: int, allow_split: bool, chunk_tokens: int) -> int:
-    if not allow_split:
-        return NO_SPLIT_CHUNK
-    if chunk_tokens > 0:
-        return _roundup(chunk_tokens, TILE)
-    per_item = _cdiv(total_tokens, num_cus * ITEMS_PER_CU) if total_tokens > 0 else 0
-    return max(MIN_CHUNK, _roundup(per_item, TILE))
-
-
 def make_plan(kv_indptr, num_cus: int, allow_split: bool = True, chunk_tokens: int = 0):
-    """Return ``(C, items, merges, n_slots)`` with items/merges as lists of 4-tuples."""
+    """Return ``(worker_segments, merges, n_slots)``; worker_segments is a list of lists."""
     indptr = [int(x) for x in kv_indptr]
     batch = len(indptr) - 1
-    c_len = chunk_length(indptr[-1], num_cus, allow_split, chunk_tokens)
-    items, merges = [], []
+    total = indptr[-1]
+    merges = []
+    if not allow_split:
+        seqs = [b for b in range(batch) if indptr[b + 1] > indptr[b]]
+        merges = [(b, 0, 0, 0) for b in range(batch) if indptr[b + 1] == indptr[b]]
+        seqs.sort(key=lambda b: (-(indptr[b + 1] - indptr[b]), b))
+        return [[(b, 0, indptr[b + 1] - indptr[b], -1)] for b in seqs], merges, 0
+
+    if total == 0:
+        workers = 0
+    elif chunk_tokens > 0:
+        workers = _cdiv(total, chunk_tokens)
+    else:
+        workers = min(num_cus * WORKERS_PER_CU, _cdiv(total, MIN_WORKER_TOKENS))
+    bounds = [w * total // workers for w in range(workers)] + [total] if workers else [0]
+    per_worker = [[] for _ in range(workers)]
     slot = 0
     for b in range(batch):
-        n = indptr[b + 1] - indptr[b]
-        if n <= c_len:
-            items.append((b, 0, n, -1))
+        lo, hi = indptr[b], indptr[b + 1]
+        if lo == hi:
+            merges.append((b, 0, 0, 0))
             continue
-        k = _cdiv(n, c_len)
-        c = _roundup(_cdiv(n, k), TILE)
-        k = _cdiv(n, c)
-        for j in range(k):
-            items.append((b, j * c, min((j + 1) * c, n), slot + j))
-        merges.append((b, slot, k, 0))
-        slot += k
-    order = sorted(range(len(items)), key=lambda i: (-(items[i][2] - items[i][1]), i))
-    items = [items[i] for i in order]
-    return c_len, items, merges, slot
+        pieces = []
+        w = bisect.bisect_right(bounds, lo) - 1          # worker holding position lo
+        while w < workers and bounds[w] < hi:
+            a, e = max(lo, bounds[w]), min(hi, bounds[w + 1])
+            if e > a:
+                pieces.append((w, a - lo, e - lo))
+            w += 1
+        if len(pieces) == 1:
+            w, a, e = pieces[0]
+            per_worker[w].append((b, a, e, -1))
+        else:
+            for j, (w, a, e) in enumerate(pieces):
+                per_worker[w].append((b, a, e, slot + j))
+            merges.append((b, slot, len(pieces), 0))
+            slot += len(pieces)
+    return per_worker, merges, slot
 
 
 def export(kv_indptr, num_cus: int, allow_split: bool = True, chunk_tokens: int = 0):
-    c_len, items, merges, slots = make_plan(kv_indptr, num_cus, allow_split, chunk_tokens)
-    flat = [c_len, len(items), len(merges), slots]
-    for it in items:
-        flat.extend(it)
+    per_worker, merges, slots = make_plan(kv_indptr, num_cus, allow_split, chunk_tokens)
+    segments = [s for ws in per_worker for s in ws]
+    flat = [len(per_worker), len(segments), len(merges), slots]
+    off = 0
+    flat.append(0)
+    for ws in per_worker:
+        off += len(ws)
+        flat.append(off)
+    for s in segments:
+        flat.extend(s)
     for m in merges:
         flat.extend(m)
     return flat

@@ -11,7 +11,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/pkv.h"
+#include "pkv.h"
 #include "kernels.h"
 #include "mla.h"
 #include "plan.h"
@@ -21,8 +21,8 @@ struct pkv_plan {
   int32_t num_qo_heads, num_kv_heads, head_dim, page_size;
   int32_t num_cus, allow_split;
   pkv::Partition part;
-  std::vector<int32_t> tables;   // items then merge records, as uploaded
-  size_t off_items, off_merges, off_part_o, off_part_lse, ws_bytes;
+  std::vector<int32_t> tables;   // worker offsets, segments, merge records, as uploaded
+  size_t off_wptr, off_segs, off_merges, off_part_o, off_part_lse, ws_bytes;
   void* workspace;               // device buffer the tables were uploaded to (or NULL)
 };
 
@@ -104,16 +104,21 @@ pkv_status make_plan(const int32_t* kv_indptr_host, int32_t batch, int32_t num_q
   p->num_cus = num_cus;
   p->allow_split = allow_split != 0;
   p->tables.clear();
-  p->tables.reserve(4 * (p->part.items.size() + p->part.merges.size()));
-  for (const auto& it : p->part.items) {
-    p->tables.insert(p->tables.end(), {it.b, it.tok_begin, it.tok_end, it.slot});
+  p->tables.reserve(p->part.worker_ptr.size() + 4 * (p->part.segments.size() + p->part.merges.size()));
+  p->tables.insert(p->tables.end(), p->part.worker_ptr.begin(), p->part.worker_ptr.end());
+  const size_t n_wptr = p->part.worker_ptr.size();
+  const size_t pad = (4 - n_wptr % 4) % 4;   // segments start 16-byte aligned
+  p->tables.insert(p->tables.end(), pad, 0);
+  for (const auto& sg : p->part.segments) {
+    p->tables.insert(p->tables.end(), {sg.b, sg.tok_begin, sg.tok_end, sg.slot});
   }
   for (const auto& m : p->part.merges) {
-    p->tables.insert(p->tables.end(), {m.b, m.first_slot, m.n_chunks, m.pad});
+    p->tables.insert(p->tables.end(), {m.b, m.first_slot, m.n_segments, m.pad});
   }
   const size_t slots = static_cast<size_t>(p->part.n_slots);
-  p->off_items = 0;
-  p->off_merges = p->off_items + 16 * p->part.items.size();
+  p->off_wptr = 0;
+  p->off_segs = 4 * (n_wptr + pad);
+  p->off_merges = p->off_segs + 16 * p->part.segments.size();
   p->off_part_o = align_up(p->off_merges + 16 * p->part.merges.size());
   p->off_part_lse = align_up(p->off_part_o + slots * num_qo_heads * head_dim * sizeof(float));
   p->ws_bytes = align_up(p->off_part_lse + slots * num_qo_heads * sizeof(float));
@@ -196,16 +201,24 @@ void pkv_plan_destroy(pkv_plan* plan) { delete plan; }
 
 pkv_status pkv_plan_export(const pkv_plan* plan, int32_t* dst, size_t n_int32, size_t* needed) {
   if (plan == nullptr) return fail(PKV_ERR_INVALID_ARG, "plan is NULL");
-  const size_t count = 4 + plan->tables.size();
+  const auto& pt = plan->part;
+  const size_t count = 4 + pt.worker_ptr.size() + 4 * (pt.segments.size() + pt.merges.size());
   if (needed != nullptr) *needed = count;
   if (dst == nullptr) return ok();
   if (n_int32 < count)
     return fail(PKV_ERR_INVALID_ARG, "export needs %zu int32 values, got %zu", count, n_int32);
-  dst[0] = plan->part.chunk;
-  dst[1] = static_cast<int32_t>(plan->part.items.size());
-  dst[2] = static_cast<int32_t>(plan->part.merges.size());
-  dst[3] = plan->part.n_slots;
-  if (!plan->tables.empty()) std::memcpy(dst + 4, plan->tables.data(), plan->tables.size() * 4);
+  int32_t* d = dst;
+  *d++ = pt.n_workers;
+  *d++ = static_cast<int32_t>(pt.segments.size());
+  *d++ = static_cast<int32_t>(pt.merges.size());
+  *d++ = pt.n_slots;
+  for (int32_t v : pt.worker_ptr) *d++ = v;
+  for (const auto& sg : pt.segments) {
+    *d++ = sg.b; *d++ = sg.tok_begin; *d++ = sg.tok_end; *d++ = sg.slot;
+  }
+  for (const auto& m : pt.merges) {
+    *d++ = m.b; *d++ = m.first_slot; *d++ = m.n_segments; *d++ = m.pad;
+  }
   return ok();
 }
 
@@ -252,13 +265,14 @@ pkv_status pkv_run(const pkv_plan* plan, const void* q, int32_t q_batch, int32_t
   if (workspace_bytes < plan->ws_bytes)
     return fail(PKV_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, plan needs %zu",
                 workspace_bytes, plan->ws_bytes);
-  if (plan->part.items.empty()) return ok();
+  if (plan->part.n_workers == 0) return ok();
 
   char* ws = static_cast<char*>(workspace);
   const float log2e = 1.4426950408889634f;
   hipError_t e = pkv::launch_decode_partial(
-      reinterpret_cast<const int32_t*>(ws + plan->off_items),
-      static_cast<int32_t>(plan->part.items.size()), static_cast<const uint16_t*>(q),
+      reinterpret_cast<const int32_t*>(ws + plan->off_wptr),
+      reinterpret_cast<const int32_t*>(ws + plan->off_segs), plan->part.n_workers,
+      static_cast<const uint16_t*>(q),
       static_cast<const uint16_t*>(k_pool), static_cast<const uint16_t*>(v_pool), kv_indptr,
       kv_indices, sm_scale * log2e, static_cast<uint16_t*>(out), lse,
       reinterpret_cast<float*>(ws + plan->off_part_o), reinterpret_cast<float*>(ws + plan->off_part_lse),

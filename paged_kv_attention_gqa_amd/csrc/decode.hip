@@ -9,8 +9,9 @@
 // qsa.py (_qsa_sparse_paged_gqa_splitk_kernel, _qsa_merge_splitk_kernel).
 //
 // Design (gfx950, wave64):
-// * One workgroup per work item (b, token range); wave w handles KV head w and
-//   its 8 query heads. A wave walks its range in tiles of 32 tokens.
+// * One workgroup per worker of the plan: an equal share of the batch's tokens,
+//   as a list of (sequence, token range) segments. Wave w handles KV head w
+//   and its 8 query heads and walks each segment in tiles of 32 tokens.
 // * Both contractions run on v_mfma_f32_16x16x32_bf16, the 8 query heads
 //   padded to 16 MFMA columns:
 //     S^T[tok, h] = K[tok, :] . Q[h, :]        A = K rows as loaded, B = Q^T
@@ -156,33 +157,19 @@ __device__ __forceinline__ void compute_tile(const Tile& t, int t0, int n, const
   }
 }
 
-__global__ __launch_bounds__(kThreads) void decode_partial_kernel(
-    const int32_t* __restrict__ items, const uint16_t* __restrict__ q,
+// Decodes tokens [lo, lo + n) of sequence b (n > 0) with all four waves of the
+// workgroup and writes either the final out/lse (slot < 0) or a partial.
+__device__ __forceinline__ void process_segment(
+    int b, int lo, int n, int slot, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k_pool, const uint16_t* __restrict__ v_pool,
     const int32_t* __restrict__ kv_indptr, const int32_t* __restrict__ kv_indices,
     float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
-    float* __restrict__ part_o, float* __restrict__ part_lse) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[kHkv * kWaveLdsU16];
+    float* __restrict__ part_o, float* __restrict__ part_lse, uint16_t* lds) {
   const int lane = threadIdx.x & 63;
   const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // KV head of this wave
   const int r = lane & 15;
   const int c = lane >> 4;
-  const int32_t* it = items + 4 * blockIdx.x;
-  const int b = it[0];
-  const int lo = it[1];
-  const int n = it[2] - lo;
-  const int slot = it[3];
   const int head = g * kGroup + r;   // a real query head only for r < kGroup
-
-  if (n == 0) {   // empty sequence: out = 0, lse = -inf
-    if (r < kGroup) {
-      uint16_t* o = out + (static_cast<int64_t>(b) * kHq + head) * kHeadDim + 4 * c;
-#pragma unroll
-      for (int db = 0; db < 8; ++db) *reinterpret_cast<u32x2*>(o + 16 * db) = u32x2{0u, 0u};
-      if (c == 0) lse[b * kHq + head] = kNegInf;
-    }
-    return;
-  }
 
   const int32_t* ids = kv_indices + kv_indptr[b] + lo;
   const int last = n - 1;
@@ -203,28 +190,41 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(
   for (int db = 0; db < 8; ++db) st.acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   st.m = kNegInf;
   st.l = 0.f;
-  uint16_t* lw = lds + g * kWaveLdsU16;
+  uint16_t* lw = lds + g * kWaveLdsU16;   // each wave owns its LDS slice
 
-  // Pipeline: ids two tiles ahead, K/V one tile ahead.
+  // Software pipeline over pairs of 32-token tiles with two register
+  // buffers: while one tile is computed the other is in flight. Page ids are
+  // fetched two tiles ahead and issued before the K/V loads of the tile
+  // after the one being computed, so waiting for them never waits for
+  // younger K/V loads. The loop body has no early exit (an odd tile count
+  // ends with one fully masked tile), and the empty asm statements keep every
+  // load group where it is written.
+  const int n_pairs = (n + 2 * kTileTok - 1) / (2 * kTileTok);
   int32_t pa0 = ids[min(r, last)];
   int32_t pa1 = ids[min(16 + r, last)];
   int32_t pb0 = ids[min(32 + r, last)];
   int32_t pb1 = ids[min(48 + r, last)];
   Tile ta, tb;
   load_tile(ta, k_pool, v_pool, pa0, pa1, g, c);
-  for (int t0 = 0;;) {
+  int t0 = 0;
+  for (int pair = 0; pair < n_pairs; ++pair) {
+    asm volatile("" ::: "memory");
     pa0 = ids[min(t0 + 64 + r, last)];
     pa1 = ids[min(t0 + 80 + r, last)];
     load_tile(tb, k_pool, v_pool, pb0, pb1, g, c);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
     compute_tile(ta, t0, n, qf, scale_log2, r, c, lw, st);
-    t0 += kTileTok;
-    if (t0 >= n) break;
-    pb0 = ids[min(t0 + 64 + r, last)];
-    pb1 = ids[min(t0 + 80 + r, last)];
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    pb0 = ids[min(t0 + 96 + r, last)];
+    pb1 = ids[min(t0 + 112 + r, last)];
     load_tile(ta, k_pool, v_pool, pa0, pa1, g, c);
-    compute_tile(tb, t0, n, qf, scale_log2, r, c, lw, st);
-    t0 += kTileTok;
-    if (t0 >= n) break;
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    compute_tile(tb, t0 + kTileTok, n, qf, scale_log2, r, c, lw, st);
+    __builtin_amdgcn_sched_barrier(0);
+    t0 += 2 * kTileTok;
   }
 
   float l_tot = st.l + __shfl_xor(st.l, 16);
@@ -253,59 +253,99 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(
   }
 }
 
-// One workgroup per split sequence: thread t merges head t/8, dims 16*(t%8) .. +16.
+// One workgroup per worker: it walks its segments in order.
+__global__ __launch_bounds__(kThreads) void decode_partial_kernel(
+    const int32_t* __restrict__ worker_ptr, const int32_t* __restrict__ segments,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
+    const uint16_t* __restrict__ v_pool, const int32_t* __restrict__ kv_indptr,
+    const int32_t* __restrict__ kv_indices, float scale_log2, uint16_t* __restrict__ out,
+    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kHkv * kWaveLdsU16];
+  const int s_end = worker_ptr[blockIdx.x + 1];
+  for (int s = worker_ptr[blockIdx.x]; s < s_end; ++s) {
+    const int32_t* seg = segments + 4 * s;
+    const int lo = seg[1];
+    const int n = seg[2] - lo;
+    if (n > 0)
+      process_segment(seg[0], lo, n, seg[3], q, k_pool, v_pool, kv_indptr, kv_indices,
+                      scale_log2, out, lse, part_o, part_lse, lds);
+  }
+}
+
+// One workgroup per (split sequence, query head). The 256 threads form 8
+// groups of 32; group j takes chunks j, j+8, j+16, ... and each lane of a group
+// owns 4 consecutive dims. The groups' partial sums are combined in LDS in a
+// fixed order, so the result does not depend on timing.
+constexpr int kMergeGroups = 8;
+
 __global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ merges,
                                                     const float* __restrict__ part_o,
                                                     const float* __restrict__ part_lse,
                                                     uint16_t* __restrict__ out,
                                                     float* __restrict__ lse) {
+  __shared__ float s_top[kMergeGroups];
+  __shared__ float s_den[kMergeGroups];
+  __shared__ f32x4 s_acc[kMergeGroups][32];
   const int32_t* m = merges + 4 * blockIdx.x;
   const int b = m[0];
   const int first = m[1];
   const int k = m[2];
-  const int h = threadIdx.x >> 3;
-  const int d0 = (threadIdx.x & 7) * 16;
+  const int h = blockIdx.y;
+  const int grp = threadIdx.x >> 5;
+  const int d0 = (threadIdx.x & 31) * 4;
 
   float top = kNegInf;
-  for (int i = 0; i < k; ++i) top = fmaxf(top, part_lse[static_cast<int64_t>(first + i) * kHq + h]);
+  for (int i = grp; i < k; i += kMergeGroups)
+    top = fmaxf(top, part_lse[static_cast<int64_t>(first + i) * kHq + h]);
+  if ((threadIdx.x & 31) == 0) s_top[grp] = top;
+  __syncthreads();
+  top = s_top[0];
+#pragma unroll
+  for (int j = 1; j < kMergeGroups; ++j) top = fmaxf(top, s_top[j]);
 
-  f32x4 acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
   if (top != kNegInf) {
-    for (int i = 0; i < k; ++i) {
-      const int64_t s = static_cast<int64_t>(first + i) * kHq + h;
-      const float li = part_lse[s];
+#pragma unroll 4
+    for (int i = grp; i < k; i += kMergeGroups) {
+      const int64_t slot = static_cast<int64_t>(first + i) * kHq + h;
+      const float li = part_lse[slot];
       const float w = (li == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(li - top);
       den += w;
-      const f32x4* src = reinterpret_cast<const f32x4*>(part_o + s * kHeadDim + d0);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] += w * src[j];
+      acc += w * *reinterpret_cast<const f32x4*>(part_o + slot * kHeadDim + d0);
     }
   }
-  const float inv = (den > 0.f) ? 1.0f / den : 0.f;
-  uint16_t* o = out + (static_cast<int64_t>(b) * kHq + h) * kHeadDim + d0;
-  u32x4 w0, w1;
+  s_acc[grp][threadIdx.x & 31] = acc;
+  if ((threadIdx.x & 31) == 0) s_den[grp] = den;
+  __syncthreads();
+  if (grp != 0) return;
+  acc = s_acc[0][threadIdx.x];
+  den = s_den[0];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t lo16 = bf16_bits(acc[j >> 1][(2 * j) & 3] * inv);
-    const uint32_t hi16 = bf16_bits(acc[j >> 1][(2 * j + 1) & 3] * inv);
-    const uint32_t word = lo16 | (hi16 << 16);
-    if (j < 4) w0[j] = word; else w1[j - 4] = word;
+  for (int j = 1; j < kMergeGroups; ++j) {
+    acc += s_acc[j][threadIdx.x];
+    den += s_den[j];
   }
-  reinterpret_cast<u32x4*>(o)[0] = w0;
-  reinterpret_cast<u32x4*>(o)[1] = w1;
-  if ((threadIdx.x & 7) == 0) lse[b * kHq + h] = (den > 0.f) ? top + __log2f(den) : kNegInf;
+  const float inv = (den > 0.f) ? 1.0f / den : 0.f;
+  const u32x2 w = {static_cast<uint32_t>(bf16_bits(acc[0] * inv)) |
+                       (static_cast<uint32_t>(bf16_bits(acc[1] * inv)) << 16),
+                   static_cast<uint32_t>(bf16_bits(acc[2] * inv)) |
+                       (static_cast<uint32_t>(bf16_bits(acc[3] * inv)) << 16)};
+  *reinterpret_cast<u32x2*>(out + (static_cast<int64_t>(b) * kHq + h) * kHeadDim + d0) = w;
+  if (threadIdx.x == 0) lse[b * kHq + h] = (den > 0.f) ? top + __log2f(den) : kNegInf;
 }
 
 }  // namespace
 
-hipError_t launch_decode_partial(const int32_t* items, int32_t n_items, const uint16_t* q,
+hipError_t launch_decode_partial(const int32_t* worker_ptr, const int32_t* segments,
+                                 int32_t n_workers, const uint16_t* q,
                                  const uint16_t* k_pool, const uint16_t* v_pool,
                                  const int32_t* kv_indptr, const int32_t* kv_indices,
                                  float sm_scale_log2, uint16_t* out, float* lse,
                                  float* part_o, float* part_lse, hipStream_t stream) {
-  if (n_items <= 0) return hipSuccess;
-  hipLaunchKernelGGL(decode_partial_kernel, dim3(n_items), dim3(kThreads), 0, stream, items, q,
+  if (n_workers <= 0) return hipSuccess;
+  hipLaunchKernelGGL(decode_partial_kernel, dim3(n_workers), dim3(kThreads), 0, stream, worker_ptr,
+                     segments, q,
                      k_pool, v_pool, kv_indptr, kv_indices, sm_scale_log2, out, lse, part_o,
                      part_lse);
   return hipGetLastError();
@@ -314,7 +354,8 @@ hipError_t launch_decode_partial(const int32_t* items, int32_t n_items, const ui
 hipError_t launch_merge(const int32_t* merges, int32_t n_merges, const float* part_o,
                         const float* part_lse, uint16_t* out, float* lse, hipStream_t stream) {
   if (n_merges <= 0) return hipSuccess;
-  hipLaunchKernelGGL(merge_kernel, dim3(n_merges), dim3(256), 0, stream, merges, part_o, part_lse,
+  hipLaunchKernelGGL(merge_kernel, dim3(n_merges, kHq), dim3(256), 0, stream, merges, part_o,
+                     part_lse,
                      out, lse);
   return hipGetLastError();
 }

@@ -15,14 +15,16 @@ constexpr int kHq = 32;
 constexpr int kHkv = 4;
 constexpr int kHeadDim = 128;
 
-// One workgroup per work item (b, tok_begin, tok_end, slot) of `items`.
-hipError_t launch_decode_partial(const int32_t* items, int32_t n_items, const uint16_t* q,
+// One workgroup per worker; worker w decodes the segments
+// segments[worker_ptr[w] .. worker_ptr[w+1]), each (b, tok_begin, tok_end, slot).
+hipError_t launch_decode_partial(const int32_t* worker_ptr, const int32_t* segments,
+                                 int32_t n_workers, const uint16_t* q,
                                  const uint16_t* k_pool, const uint16_t* v_pool,
                                  const int32_t* kv_indptr, const int32_t* kv_indices,
                                  float sm_scale_log2, uint16_t* out, float* lse,
                                  float* part_o, float* part_lse, hipStream_t stream);
 
-// One workgroup per merge record (b, first_slot, n_chunks, 0).
+// One workgroup per (merge record (b, first_slot, n_segments, 0), query head).
 hipError_t launch_merge(const int32_t* merges, int32_t n_merges, const float* part_o,
                         const float* part_lse, uint16_t* out, float* lse, hipStream_t stream);
 

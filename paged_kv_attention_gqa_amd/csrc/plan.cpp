@@ -8,7 +8,6 @@ namespace pkv {
 namespace {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
-int64_t roundup(int64_t a, int64_t m) { return cdiv(a, m) * m; }
 
 }  // namespace
 
@@ -27,49 +26,77 @@ bool build_partition(const int32_t* kv_indptr, int32_t batch, int32_t num_cus,
   if (chunk_tokens < 0) { *err = "chunk_tokens must be >= 0"; return false; }
 
   Partition p;
-  p.total_tokens = kv_indptr[batch];
-  int64_t chunk;
-  if (!allow_split) {
-    chunk = kNoSplitChunk;
-  } else if (chunk_tokens > 0) {
-    chunk = roundup(chunk_tokens, kTile);
-  } else {
-    const int64_t per_item =
-        p.total_tokens > 0 ? cdiv(p.total_tokens, int64_t(num_cus) * kItemsPerCu) : 0;
-    chunk = std::max<int64_t>(kMinChunk, roundup(per_item, kTile));
-  }
-  if (chunk > kNoSplitChunk) chunk = kNoSplitChunk;
-  p.chunk = static_cast<int32_t>(chunk);
+  const int64_t total = kv_indptr[batch];
+  p.total_tokens = total;
 
-  std::vector<WorkItem> made;
-  made.reserve(static_cast<size_t>(batch) + static_cast<size_t>(p.total_tokens / chunk) + 1);
+  if (!allow_split) {
+    // One worker per non-empty sequence, longest first; empty sequences are
+    // merge records with no segments.
+    std::vector<int32_t> order;
+    for (int32_t b = 0; b < batch; ++b) {
+      if (kv_indptr[b + 1] > kv_indptr[b]) order.push_back(b);
+      else p.merges.push_back({b, 0, 0, 0});
+    }
+    std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
+      return kv_indptr[x + 1] - kv_indptr[x] > kv_indptr[y + 1] - kv_indptr[y];
+    });
+    p.worker_ptr.push_back(0);
+    for (int32_t b : order) {
+      p.segments.push_back({b, 0, kv_indptr[b + 1] - kv_indptr[b], -1});
+      p.worker_ptr.push_back(static_cast<int32_t>(p.segments.size()));
+    }
+    p.n_workers = static_cast<int32_t>(order.size());
+    *out = std::move(p);
+    return true;
+  }
+
+  int64_t workers;
+  if (total == 0) {
+    workers = 0;
+  } else if (chunk_tokens > 0) {
+    workers = cdiv(total, chunk_tokens);
+  } else {
+    workers = std::min<int64_t>(int64_t(num_cus) * kWorkersPerCu, cdiv(total, kMinWorkerTokens));
+  }
+  p.n_workers = static_cast<int32_t>(workers);
+  // Worker w owns the tokens [w*total/workers, (w+1)*total/workers).
+  auto start = [&](int64_t w) { return w * total / workers; };
+
+  std::vector<std::vector<Segment>> per_worker(static_cast<size_t>(workers));
   int32_t slot = 0;
   for (int32_t b = 0; b < batch; ++b) {
-    const int64_t n = int64_t(kv_indptr[b + 1]) - kv_indptr[b];
-    if (n <= chunk) {
-      made.push_back({b, 0, static_cast<int32_t>(n), -1});
+    const int64_t lo = kv_indptr[b], hi = kv_indptr[b + 1];
+    if (hi == lo) {
+      p.merges.push_back({b, 0, 0, 0});
       continue;
     }
-    int64_t k = cdiv(n, chunk);
-    const int64_t c = roundup(cdiv(n, k), kTile);
-    k = cdiv(n, c);
-    for (int64_t j = 0; j < k; ++j) {
-      made.push_back({b, static_cast<int32_t>(j * c), static_cast<int32_t>(std::min((j + 1) * c, n)),
-                      static_cast<int32_t>(slot + j)});
+    // first worker whose range contains lo: largest w with start(w) <= lo
+    int64_t w = std::min<int64_t>(workers - 1, (lo * workers) / total);
+    while (w > 0 && start(w) > lo) --w;
+    while (w + 1 < workers && start(w + 1) <= lo) ++w;
+    const bool single = hi <= start(w + 1);
+    int32_t k = 0;
+    for (int64_t pos = lo; pos < hi; ++w) {
+      const int64_t end = std::min<int64_t>(hi, start(w + 1));
+      if (end > pos) {
+        per_worker[static_cast<size_t>(w)].push_back(
+            {b, static_cast<int32_t>(pos - lo), static_cast<int32_t>(end - lo),
+             single ? -1 : slot + k});
+        ++k;
+      }
+      pos = end;
     }
-    p.merges.push_back({b, slot, static_cast<int32_t>(k), 0});
-    slot += static_cast<int32_t>(k);
+    if (!single) {
+      p.merges.push_back({b, slot, k, 0});
+      slot += k;
+    }
   }
   p.n_slots = slot;
-  // Longest items first so that the tail of the launch holds the short ones;
-  // equal lengths keep their creation order.
-  std::vector<size_t> order(made.size());
-  std::iota(order.begin(), order.end(), size_t(0));
-  std::stable_sort(order.begin(), order.end(), [&](size_t x, size_t y) {
-    return (made[x].tok_end - made[x].tok_begin) > (made[y].tok_end - made[y].tok_begin);
-  });
-  p.items.reserve(made.size());
-  for (size_t i : order) p.items.push_back(made[i]);
+  p.worker_ptr.push_back(0);
+  for (auto& segs : per_worker) {
+    p.segments.insert(p.segments.end(), segs.begin(), segs.end());
+    p.worker_ptr.push_back(static_cast<int32_t>(p.segments.size()));
+  }
   *out = std::move(p);
   return true;
 }

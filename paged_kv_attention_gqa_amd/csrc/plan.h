@@ -1,12 +1,17 @@
 // Split-KV work partition for paged decode (host only, no HIP).
 //
-// A batch is cut into work items (b, tok_begin, tok_end, slot). Items of a
-// sequence that fits one chunk write the final output (slot = -1); longer
-// sequences are cut into equal tile-rounded chunks whose fp32 partials go to
-// consecutive workspace slots and are combined by one merge record
-// (b, first_slot, n_chunks, 0). The idea of splitting one row's keys into
-// contiguous tiles with no empty split and merging by LSE is the vLLM fork
-// qsa.py's (qsa_sparse_paged_attention); the chunk rule is this library's.
+// The batch's tokens, taken in kv_indices order, are cut into equal
+// contiguous ranges, one per worker (one workgroup of the decode kernel).
+// A worker's range is a list of segments (b, tok_begin, tok_end, slot), one
+// per sequence it touches, with token positions relative to the sequence. A
+// sequence that lies inside one worker is written directly (slot = -1); a
+// sequence cut across workers leaves one normalised fp32 partial per segment
+// in consecutive workspace slots, combined by a merge record
+// (b, first_slot, n_segments, 0). Empty sequences get a merge record with no
+// segments, which writes zeros and -inf. Splitting one row's keys into
+// contiguous pieces with no empty piece and merging by LSE is the vLLM fork
+// qsa.py's idea (qsa_sparse_paged_attention); the partition rule is this
+// library's.
 #ifndef PKV_PLAN_H_
 #define PKV_PLAN_H_
 
@@ -16,28 +21,30 @@
 
 namespace pkv {
 
-constexpr int32_t kTile = 32;          // tokens per kernel tile; chunk lengths are multiples
-constexpr int32_t kMinChunk = 256;     // shortest automatic chunk
-constexpr int32_t kItemsPerCu = 2;     // automatic chunk aims at this many items per CU
-constexpr int32_t kNoSplitChunk = 2147483647;
+constexpr int32_t kWorkersPerCu = 2;       // decode workgroups resident per CU
+constexpr int32_t kMinWorkerTokens = 128;  // fewest tokens given to one worker
 
-struct WorkItem {
+struct Segment {
   int32_t b, tok_begin, tok_end, slot;
 };
 struct MergeItem {
-  int32_t b, first_slot, n_chunks, pad;
+  int32_t b, first_slot, n_segments, pad;
 };
 
 struct Partition {
-  int32_t chunk = 0;
+  int32_t n_workers = 0;
   int32_t n_slots = 0;
   int64_t total_tokens = 0;
-  std::vector<WorkItem> items;
+  std::vector<int32_t> worker_ptr;   // n_workers + 1 offsets into segments
+  std::vector<Segment> segments;
   std::vector<MergeItem> merges;
 };
 
-// Checks kv_indptr (starts at 0, non-decreasing, total < 2^31) and builds the
-// partition. Returns false with a message in *err on bad input.
+// Checks kv_indptr (starts at 0, non-decreasing) and builds the partition.
+// allow_split = false gives one worker per sequence. chunk_tokens > 0 sets
+// the tokens per worker; 0 chooses num_cus * kWorkersPerCu workers (fewer
+// when the batch has under kMinWorkerTokens tokens per worker). Returns false
+// with a message in *err on bad input.
 bool build_partition(const int32_t* kv_indptr, int32_t batch, int32_t num_cus,
                      bool allow_split, int32_t chunk_tokens, Partition* out, std::string* err);
 

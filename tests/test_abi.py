@@ -95,9 +95,11 @@ def test_workspace_size_formula(lib):
     ind = _indptr([1000, 10, 0, 5000])
     st, n = _ws(ind, chunk=256)
     assert st == pkv.PKV_OK
-    c_len, items, merges, slots = plan_ref.make_plan(ind, 256, True, 256)
+    per_worker, merges, slots = plan_ref.make_plan(ind, 256, True, 256)
     al = lambda x: -(-x // 256) * 256
-    tables = 16 * (len(items) + len(merges))
+    n_wptr = len(per_worker) + 1
+    segs = sum(len(s) for s in per_worker)
+    tables = 4 * (n_wptr + (-n_wptr) % 4) + 16 * (segs + len(merges))
     part_o = al(tables)
     part_lse = al(part_o + slots * 32 * 128 * 4)
     assert n == al(part_lse + slots * 32 * 4)
@@ -120,7 +122,8 @@ PLAN_CASES = [
 
 @pytest.mark.parametrize("name,ind", PLAN_CASES, ids=[c[0] for c in PLAN_CASES])
 @pytest.mark.parametrize("cus,split,chunk", [(256, True, 0), (256, False, 0), (80, True, 0),
-                                             (256, True, 64), (1, True, 0), (304, True, 1000)])
+                                             (256, True, 64), (1, True, 0), (304, True, 1000),
+                                             (256, True, 7)])
 def test_plan_export_matches_rule(lib, name, ind, cus, split, chunk):
     assert _host_plan(ind, cus, split, chunk) == plan_ref.export(ind, cus, split, chunk)
 
@@ -132,7 +135,7 @@ def test_plan_export_random(lib, seed):
     lengths = rng.integers(0, 40000, size=batch) * (rng.random(batch) < 0.8)
     ind = _indptr(lengths)
     cus = int(rng.choice([1, 7, 256, 304]))
-    chunk = int(rng.choice([0, 0, 0, 1, 33, 512]))
+    chunk = int(rng.choice([0, 0, 0, 33, 512]))
     split = bool(rng.random() < 0.9)
     assert _host_plan(ind, cus, split, chunk) == plan_ref.export(ind, cus, split, chunk)
 

@@ -14,6 +14,9 @@ namespace pkv {
 constexpr int kMlaDqk = 576;
 constexpr int kMlaDv = 512;
 constexpr int kMlaMaxHeads = 128;
+// The list is cut into pieces so that about this many workgroups run; fixed so
+// that the workspace size depends on the shape only.
+constexpr int kMlaPlanCus = 256;
 
 // Checks the gather shape; returns 0 and the workspace size, or a pkv_status
 // code with a message.

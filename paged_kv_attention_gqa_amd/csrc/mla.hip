@@ -1,10 +1,292 @@
-// Index-gather latent-attention decode for gfx950 (placeholder launcher; the
-// kernel is not built yet and the launcher reports hipErrorNotSupported).
+// Index-gather latent-attention decode for gfx950 (MI355X).
+//
+// What is computed follows the FlagGems flash_mla_with_kvcache page
+// (_sparse_decode_kernel, bf16 mode): for row b every list entry
+// t = indices[b, i] with 0 <= t < pool_tokens selects pool row kv[t]
+// (576 bf16: scores use all 576 dims, values are the first 512 dims); other
+// entries are masked. Scores are scaled by sm_scale, reduced with an online
+// softmax, and the output is bf16 with a base-2 LSE.
+//
+// Design:
+// * Work is split three ways: row b, a block of up to 64 query heads, and a
+//   contiguous piece of the index list; one workgroup (4 waves) per triple,
+//   wave w owning 16 heads. Pieces of one (row, head block) leave normalised
+//   fp32 partials that a second kernel merges by LSE (vLLM fork qsa.py,
+//   _qsa_merge_splitk_kernel); with a single piece the output is final.
+// * 128 heads share every gathered row, so both contractions are dense and
+//   run on v_mfma_f32_16x16x32_bf16:
+//     S^T[tok, h] = K[tok, :] . Q[h, :]        A = K rows from LDS, B = Q^T (registers)
+//     O^T[d, h]  += V^T[d, tok] . P^T[tok, h]  A = V^T read with ds_read_b64_tr_b16
+//   The transposing LDS read hands each lane four tokens of one dim, so V is
+//   never rewritten transposed. The S^T accumulator already holds each lane's
+//   P^T operand (head = lane % 16, tokens 16h + 4c + j), as in the GQA kernel.
+// * A tile is 32 gathered rows (36 KB): eight threads per row load it with
+//   16-byte loads (eight lanes cover 128 contiguous bytes) into registers one
+//   tile ahead of the compute (list entries two tiles ahead), then store it to
+//   one of two LDS buffers whose rows are padded to 1168 bytes, conflict-free
+//   for both LDS read patterns.
+// * A masked entry loads row 0 (so the data is finite) and gets score -inf.
+//   A piece with no valid entry gives out 0 and lse -inf.
 #include <hip/hip_runtime.h>
 
 #include "mla.h"
 
 namespace pkv {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTileTok = 32;
+constexpr int kUnitsPerRow = kMlaDqk / 8;          // 72 units of 16 bytes
+constexpr int kRowU16 = kMlaDqk + 8;               // LDS row: 1152 B + 16 B pad
+constexpr int kBufU16 = kTileTok * kRowU16;        // one tile buffer
+constexpr int kThreads = 256;
+constexpr int kLoadsPerThread = kTileTok * kUnitsPerRow / kThreads;   // 9
+constexpr int kHeadsPerWave = 16;
+constexpr int kHeadBlock = 4 * kHeadsPerWave;      // 64 heads per workgroup
+constexpr int kQSteps = kMlaDqk / 32;              // 18 k-steps of 32 dims
+constexpr int kVBlocks = kMlaDv / 16;              // 32 blocks of 16 dims
+constexpr float kNegInf = -__builtin_huge_valf();
+static_assert(kTileTok * kUnitsPerRow % kThreads == 0, "tile must split evenly");
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+
+__device__ __forceinline__ uint16_t bf16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+// Thread t stages tile row t / 8: 16-byte units (t % 8) + 8 u, u = 0..8, so
+// eight consecutive lanes read 128 contiguous bytes of one row and every
+// thread needs a single list entry per tile.
+constexpr int kThreadsPerRow = kThreads / kTileTok;   // 8
+
+struct Staged {
+  u32x4 v[kLoadsPerThread];
+  bool valid;
+};
+
+// Entry of this thread's row in the tile starting at t0 (-1 past the piece).
+__device__ __forceinline__ int32_t tile_entry(const int32_t* __restrict__ idx, int t0, int n) {
+  const int tok = t0 + static_cast<int>(threadIdx.x) / kThreadsPerRow;
+  return tok < n ? idx[tok] : -1;
+}
+
+__device__ __forceinline__ void load_tile(Staged& s, int32_t id, int64_t pool_tokens,
+                                          const uint16_t* __restrict__ kv) {
+  s.valid = id >= 0 && static_cast<int64_t>(id) < pool_tokens;
+  const uint16_t* src = kv + static_cast<int64_t>(s.valid ? id : 0) * kMlaDqk +
+                        (threadIdx.x % kThreadsPerRow) * 8;
+#pragma unroll
+  for (int u = 0; u < kLoadsPerThread; ++u)
+    s.v[u] = *reinterpret_cast<const u32x4*>(src + u * kThreadsPerRow * 8);
+}
+
+__device__ __forceinline__ void store_tile(const Staged& s, uint16_t* buf, uint8_t* vflag) {
+  const int row = threadIdx.x / kThreadsPerRow;
+  uint16_t* dst = buf + row * kRowU16 + (threadIdx.x % kThreadsPerRow) * 8;
+#pragma unroll
+  for (int u = 0; u < kLoadsPerThread; ++u)
+    *reinterpret_cast<u32x4*>(dst + u * kThreadsPerRow * 8) = s.v[u];
+  if (threadIdx.x % kThreadsPerRow == 0) vflag[row] = s.valid ? 1 : 0;
+}
+
+struct State {
+  f32x4 acc[kVBlocks];   // acc[db][i] = O[head r][16 db + 4c + i]
+  float m;               // running max (log2 domain), equal on the 4 lane rows
+  float l;               // this lane's share of the exp-sum
+};
+
+__device__ __forceinline__ void compute_tile(const uint16_t* buf, const uint8_t* vflag,
+                                             const u32x4 (&qf)[kQSteps], float scale_log2,
+                                             int r, int c, State& st) {
+  // Four independent accumulator chains (rows 0-15 / 16-31, even / odd k-steps)
+  // keep consecutive MFMAs from waiting on each other.
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s0b = s0, s1 = s0, s1b = s0;
+  const uint16_t* row0 = buf + r * kRowU16 + 8 * c;
+  const uint16_t* row1 = buf + (16 + r) * kRowU16 + 8 * c;
+#pragma unroll
+  for (int ks = 0; ks < kQSteps; ks += 2) {
+    const u32x4 k0 = *reinterpret_cast<const u32x4*>(row0 + 32 * ks);
+    const u32x4 k1 = *reinterpret_cast<const u32x4*>(row1 + 32 * ks);
+    const u32x4 k2 = *reinterpret_cast<const u32x4*>(row0 + 32 * ks + 32);
+    const u32x4 k3 = *reinterpret_cast<const u32x4*>(row1 + 32 * ks + 32);
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k0), as_bf16x8(qf[ks]), s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k1), as_bf16x8(qf[ks]), s1, 0, 0, 0);
+    s0b = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k2), as_bf16x8(qf[ks + 1]), s0b, 0, 0, 0);
+    s1b = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k3), as_bf16x8(qf[ks + 1]), s1b, 0, 0, 0);
+  }
+  s0 += s0b;
+  s1 += s1b;
+  // p[4h + j] belongs to tile row 16h + 4c + j.
+  float p[8];
+  float mx = kNegInf;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    p[j] = vflag[4 * c + j] ? s0[j] * scale_log2 : kNegInf;
+    p[4 + j] = vflag[16 + 4 * c + j] ? s1[j] * scale_log2 : kNegInf;
+    mx = fmaxf(mx, fmaxf(p[j], p[4 + j]));
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(st.m, mx);
+  const float m_use = (m_new == kNegInf) ? 0.f : m_new;   // no valid entry yet
+  const float alpha = __builtin_amdgcn_exp2f(st.m - m_use);
+  float psum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    p[j] = __builtin_amdgcn_exp2f(p[j] - m_use);
+    psum += p[j];
+  }
+  st.l = st.l * alpha + psum;
+  st.m = m_new;
+  if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {   // skip when no head's max moved
+#pragma unroll
+    for (int db = 0; db < kVBlocks; ++db) st.acc[db] *= alpha;
+  }
+  bf16x8 pb;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) pb[j] = static_cast<__bf16>(p[j]);
+
+  // V^T operand: lane (r, c) needs dim 16 db + r of tile rows 16h + 4c + j.
+  // Within each 16-lane group the transposing read gives lane i element i%4
+  // of the 8-byte chunks addressed by lanes 4j + i/4, so lane (r, c) points at
+  // row 16h + 4c + r/4, dims 16 db + 4 (r%4) .. +4.
+  const uint16_t* vrow0 = buf + (4 * c + (r >> 2)) * kRowU16 + 4 * (r & 3);
+  const uint16_t* vrow1 = vrow0 + 16 * kRowU16;
+#pragma unroll
+  for (int db = 0; db < kVBlocks; ++db) {
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(vrow0 + 16 * db));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(vrow1 + 16 * db));
+    const u32x4 a = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                     __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
+    st.acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), pb, st.acc[db], 0, 0, 0);
+  }
+}
+
+// grid: (pieces, head blocks, batch). Each workgroup decodes list entries
+// [piece * per_piece, +per_piece) of row b for heads [64 hb, 64 hb + 64).
+__global__ __launch_bounds__(kThreads) void mla_partial_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, int64_t pool_tokens,
+    const int32_t* __restrict__ indices, int topk, int num_qo_heads, int per_piece,
+    float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
+    float* __restrict__ part_o, float* __restrict__ part_lse) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kBufU16];
+  __shared__ uint8_t vflag[2][kTileTok];
+  const int piece = blockIdx.x;
+  const int hb = blockIdx.y;
+  const int b = blockIdx.z;
+  const int pieces = gridDim.x;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int r = lane & 15;
+  const int c = lane >> 4;
+  const int head = hb * kHeadBlock + w * kHeadsPerWave + r;
+  const bool head_ok = head < num_qo_heads;
+  const int t_begin = piece * per_piece;
+  const int n = min(per_piece, topk - t_begin);   // entries of this piece (may be <= 0)
+  const int32_t* idx = indices + static_cast<int64_t>(b) * topk + t_begin;
+
+  u32x4 qf[kQSteps];
+  {
+    const uint16_t* qh = q + (static_cast<int64_t>(b) * num_qo_heads + (head_ok ? head : 0)) * kMlaDqk + 8 * c;
+#pragma unroll
+    for (int ks = 0; ks < kQSteps; ++ks)
+      qf[ks] = head_ok ? *reinterpret_cast<const u32x4*>(qh + 32 * ks) : u32x4{0u, 0u, 0u, 0u};
+  }
+  State st;
+#pragma unroll
+  for (int db = 0; db < kVBlocks; ++db) st.acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m = kNegInf;
+  st.l = 0.f;
+
+  // Pipeline: list entries two tiles ahead, row data one tile ahead.
+  const int n_tiles = n > 0 ? (n + kTileTok - 1) / kTileTok : 0;
+  Staged s;
+  int32_t id_next = 0;
+  if (n_tiles > 0) {
+    load_tile(s, tile_entry(idx, 0, n), pool_tokens, kv);
+    id_next = tile_entry(idx, kTileTok, n);
+  }
+  for (int t = 0; t < n_tiles; ++t) {
+    uint16_t* buf = lds + (t & 1) * kBufU16;
+    const int32_t id_after = tile_entry(idx, (t + 2) * kTileTok, n);
+    store_tile(s, buf, vflag[t & 1]);
+    if (t + 1 < n_tiles) load_tile(s, id_next, pool_tokens, kv);
+    id_next = id_after;
+    __syncthreads();   // tile t is in LDS; every wave is done with tile t-1's buffer
+    if (hb * kHeadBlock + w * kHeadsPerWave < num_qo_heads)
+      compute_tile(buf, vflag[t & 1], qf, scale_log2, r, c, st);
+  }
+
+  float l_tot = st.l + __shfl_xor(st.l, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  const bool any = l_tot > 0.f;
+  const float inv = any ? 1.0f / l_tot : 0.f;
+  const float lse2 = any ? st.m + __log2f(l_tot) : kNegInf;
+  if (!head_ok) return;
+  if (pieces == 1) {
+    uint16_t* o = out + (static_cast<int64_t>(b) * num_qo_heads + head) * kMlaDv + 4 * c;
+#pragma unroll
+    for (int db = 0; db < kVBlocks; ++db) {
+      const f32x4 v = st.acc[db] * inv;
+      const u32x2 wds = {static_cast<uint32_t>(bf16_bits(v[0])) | (static_cast<uint32_t>(bf16_bits(v[1])) << 16),
+                         static_cast<uint32_t>(bf16_bits(v[2])) | (static_cast<uint32_t>(bf16_bits(v[3])) << 16)};
+      *reinterpret_cast<u32x2*>(o + 16 * db) = wds;
+    }
+    if (c == 0) lse[static_cast<int64_t>(b) * num_qo_heads + head] = lse2;
+  } else {
+    const int64_t slot = (static_cast<int64_t>(b) * num_qo_heads + head) * pieces + piece;
+    float* o = part_o + slot * kMlaDv + 4 * c;
+#pragma unroll
+    for (int db = 0; db < kVBlocks; ++db) *reinterpret_cast<f32x4*>(o + 16 * db) = st.acc[db] * inv;
+    if (c == 0) part_lse[slot] = lse2;
+  }
+}
+
+// One 128-thread workgroup per (row, head): thread t owns dims 4t .. 4t+3 and
+// folds the pieces in order.
+__global__ __launch_bounds__(128) void mla_merge_kernel(const float* __restrict__ part_o,
+                                                        const float* __restrict__ part_lse,
+                                                        int pieces, uint16_t* __restrict__ out,
+                                                        float* __restrict__ lse) {
+  const int64_t bh = blockIdx.x;
+  const float* pl = part_lse + bh * pieces;
+  float top = kNegInf;
+  for (int i = 0; i < pieces; ++i) top = fmaxf(top, pl[i]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  if (top != kNegInf) {
+    for (int i = 0; i < pieces; ++i) {
+      const float li = pl[i];
+      const float wgt = (li == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(li - top);
+      den += wgt;
+      acc += wgt * *reinterpret_cast<const f32x4*>(part_o + (bh * pieces + i) * kMlaDv + 4 * threadIdx.x);
+    }
+  }
+  const float inv = den > 0.f ? 1.0f / den : 0.f;
+  const u32x2 wds = {static_cast<uint32_t>(bf16_bits(acc[0] * inv)) | (static_cast<uint32_t>(bf16_bits(acc[1] * inv)) << 16),
+                     static_cast<uint32_t>(bf16_bits(acc[2] * inv)) | (static_cast<uint32_t>(bf16_bits(acc[3] * inv)) << 16)};
+  *reinterpret_cast<u32x2*>(out + bh * kMlaDv + 4 * threadIdx.x) = wds;
+  if (threadIdx.x == 0) lse[bh] = den > 0.f ? top + __log2f(den) : kNegInf;
+}
+
+// Pieces per (row, head block): enough workgroups to give each CU one, with
+// at least two tiles per piece.
+int mla_pieces(int32_t batch, int32_t num_qo_heads, int32_t topk, int num_cus) {
+  const int hblocks = (num_qo_heads + kHeadBlock - 1) / kHeadBlock;
+  const int base = max(1, batch * hblocks);
+  int pieces = max(1, (num_cus + base - 1) / base);
+  const int max_pieces = max(1, topk / (2 * kTileTok));
+  return min(pieces, max_pieces);
+}
+
+}  // namespace
 
 int mla_workspace_bytes(int32_t batch, int32_t num_qo_heads, int32_t d_qk, int32_t d_v,
                         int32_t topk, size_t* bytes, std::string* err) {
@@ -17,13 +299,30 @@ int mla_workspace_bytes(int32_t batch, int32_t num_qo_heads, int32_t d_qk, int32
     *err = "num_qo_heads must be a multiple of 16 in [16, 128]";
     return 2;
   }
-  *bytes = 0;
+  const int pieces = mla_pieces(batch, num_qo_heads, topk, kMlaPlanCus);
+  *bytes = pieces > 1 ? static_cast<size_t>(batch) * num_qo_heads * pieces * (kMlaDv + 1) * sizeof(float) : 0;
   return 0;
 }
 
-hipError_t launch_gather_mla(const uint16_t*, const uint16_t*, int64_t, const int32_t*, int32_t,
-                             int32_t, int32_t, float, void*, uint16_t*, float*, hipStream_t) {
-  return hipErrorNotSupported;
+hipError_t launch_gather_mla(const uint16_t* q, const uint16_t* kv_pool, int64_t pool_tokens,
+                             const int32_t* indices, int32_t topk, int32_t batch,
+                             int32_t num_qo_heads, float sm_scale, void* workspace,
+                             uint16_t* out, float* lse, hipStream_t stream) {
+  if (batch == 0) return hipSuccess;
+  const int pieces = mla_pieces(batch, num_qo_heads, topk, kMlaPlanCus);
+  const int per_piece = topk > 0 ? ((topk + pieces - 1) / pieces + kTileTok - 1) / kTileTok * kTileTok : 0;
+  const int hblocks = (num_qo_heads + kHeadBlock - 1) / kHeadBlock;
+  float* part_o = static_cast<float*>(workspace);
+  float* part_lse = pieces > 1 ? part_o + static_cast<size_t>(batch) * num_qo_heads * pieces * kMlaDv : nullptr;
+  const float scale_log2 = sm_scale * 1.4426950408889634f;
+  hipLaunchKernelGGL(mla_partial_kernel, dim3(pieces, hblocks, batch), dim3(kThreads), 0, stream, q,
+                     kv_pool, pool_tokens, indices, topk, num_qo_heads, per_piece, scale_log2, out,
+                     lse, part_o, part_lse);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || pieces == 1) return e;
+  hipLaunchKernelGGL(mla_merge_kernel, dim3(batch * num_qo_heads), dim3(kMlaDv / 4), 0, stream,
+                     part_o, part_lse, pieces, out, lse);
+  return hipGetLastError();
 }
 
 }  // namespace pkv

@@ -1,0 +1,75 @@
+"""Index-gather latent-attention decode on the GPU against the fp64 oracle.
+
+Tolerances: |out - ref| <= 1e-2 + 1e-2 |ref| per element, |lse - ref| <= 1e-3,
+-inf exactly where the oracle has -inf (rows with no valid entry).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_attention_gqa_amd as pkv
+from gpu_util import assert_lse_close, assert_out_close, bf16_to_np, to_dev
+from inputs import make_config, make_mla
+from oracle import ref
+
+pytestmark = pytest.mark.gpu
+
+
+def run_gpu(w, indices=None):
+    idx = w.indices if indices is None else indices
+    out, lse = pkv.gather_mla(to_dev(w.q), to_dev(w.kv_pool), to_dev(np.ascontiguousarray(idx)),
+                              w.sm_scale, d_v=w.d_v)
+    torch.cuda.synchronize()
+    return bf16_to_np(out), lse.cpu().numpy().astype(np.float64)
+
+
+def check(w, got, indices=None, what="mla"):
+    idx = w.indices if indices is None else indices
+    want = ref.mla_gather_decode(w.q, w.kv_pool, idx, w.sm_scale, w.d_v)
+    assert_out_close(got[0], want[0], what + " out")
+    assert_lse_close(got[1], want[1], what + " lse")
+
+
+def test_mla_config():
+    w = make_config("mla")
+    check(w, run_gpu(w), what="mla config")
+
+
+@pytest.mark.parametrize("heads", [16, 32, 48, 64, 128])
+@pytest.mark.parametrize("topk", [1, 31, 32, 33, 100, 640])
+def test_mla_shapes(heads, topk):
+    w = make_mla(40 + topk, batch=3, num_qo_heads=heads, pool_tokens=4096, topk=topk,
+                 masked_per_row=topk // 7)
+    check(w, run_gpu(w), what=f"heads={heads} topk={topk}")
+
+
+def test_mla_masking_rules():
+    w = make_mla(51, batch=4, num_qo_heads=64, pool_tokens=1000, topk=200, masked_per_row=20)
+    idx = w.indices.copy()
+    idx[0, :] = -1                                  # nothing valid: zeros and -inf
+    idx[1, ::3] = w.pool_tokens + 5                 # ids past the pool end are masked
+    idx[2, 10:20] = idx[2, 0]                       # repeated ids each count
+    idx[3, :] = -7
+    idx[3, 150] = 3                                 # a single valid entry
+    got = run_gpu(w, idx)
+    check(w, got, idx, "masking")
+    assert np.all(got[0][0] == 0.0) and np.all(np.isneginf(got[1][0]))
+    single = ref.bf16_to_f64(w.kv_pool[3, :w.d_v])
+    assert np.max(np.abs(got[0][3] - single)) <= 1e-2
+
+
+def test_mla_scale_and_rerun():
+    w = make_mla(52, batch=2, num_qo_heads=128, pool_tokens=3000, topk=512, sm_scale=0.11)
+    a = run_gpu(w)
+    check(w, a, what="scale")
+    b = run_gpu(w)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_mla_shape_errors():
+    w = make_mla(53, batch=1, num_qo_heads=16, pool_tokens=100, topk=8)
+    q = to_dev(w.q)
+    with pytest.raises(ValueError):
+        pkv.gather_mla(q[:, :, :512].contiguous(), to_dev(w.kv_pool)[:, :512].contiguous(),
+                       to_dev(w.indices), w.sm_scale, d_v=512)

@@ -155,16 +155,17 @@ def pkv_workspace_size(kv_indptr_host, num_qo_heads=32, num_kv_heads=4, head_dim
 
 
 class Plan:
-    """Owns one pkv_plan handle (destroyed with the object)."""
+    """Owns one pkv_plan handle (destroyed with the object, by the library that made it)."""
 
     def __init__(self, handle: int, batch: int, total_tokens: int):
         self.handle = handle
         self.batch = batch
         self.total_tokens = total_tokens
+        self._lib = lib()
 
     def __del__(self):
-        if getattr(self, "handle", None) and _LIB is not None:
-            _LIB.pkv_plan_destroy(self.handle)
+        if getattr(self, "handle", None):
+            self._lib.pkv_plan_destroy(self.handle)
             self.handle = None
 
 
@@ -187,7 +188,7 @@ def pkv_plan_create(kv_indptr_host, num_qo_heads=32, num_kv_heads=4, head_dim=12
 
 def pkv_plan_destroy(plan: Plan):
     if plan.handle:
-        lib().pkv_plan_destroy(plan.handle)
+        plan._lib.pkv_plan_destroy(plan.handle)
         plan.handle = None
 
 

@@ -10,7 +10,11 @@ LSE ([QSA page] ``qsa_sparse_paged_attention`` and its split-K kernel). The
 exact rule is this library's own and is stated here once:
 
 * The batch's ``N = kv_indptr[B]`` tokens, in ``kv_indices`` order, go to
-  ``W`` workers; worker ``w`` owns positions ``[w*N//W, (w+1)*N//W)``.
+  ``W`` workers; worker ``w`` owns positions ``[s_w, s_(w+1))`` with
+  ``s_w = w*N//W``. When ``N//W >= SNAP_MIN_SHARE``, every interior ``s_w`` is
+  moved to the nearest (ties: lower) position ``indptr[b] + TILE*k`` inside
+  the sequence ``b`` that holds it (``indptr[b] <= s_w < indptr[b+1]``),
+  capped at ``indptr[b+1]``, so that a sequence's pieces are whole tiles.
   ``W = ceil(N / chunk_tokens)`` when ``chunk_tokens > 0``, else
   ``min(num_cus * WORKERS_PER_CU, ceil(N / MIN_WORKER_TOKENS))``; ``W = 0``
   when ``N = 0``.
@@ -35,10 +39,19 @@ import bisect
 
 WORKERS_PER_CU = 2
 MIN_WORKER_TOKENS = 128
+TILE = 32
+SNAP_MIN_SHARE = 64
 
 
 def _cdiv(a: int, b: int) -> int:
     return -(-a // b)
+
+
+def round_half_down(x: float) -> int:
+    """Nearest integer, halves rounded down (x >= 0)."""
+    import math
+    f = math.floor(x)
+    return f + 1 if x - f > 0.5 else f
 
 
 def make_plan(kv_indptr, num_cus: int, allow_split: bool = True, chunk_tokens: int = 0):
@@ -60,6 +73,12 @@ def make_plan(kv_indptr, num_cus: int, allow_split: bool = True, chunk_tokens: i
     else:
         workers = min(num_cus * WORKERS_PER_CU, _cdiv(total, MIN_WORKER_TOKENS))
     bounds = [w * total // workers for w in range(workers)] + [total] if workers else [0]
+    if workers > 1 and total // workers >= SNAP_MIN_SHARE:
+        for w in range(1, workers):
+            pos = bounds[w]
+            b = bisect.bisect_right(indptr, pos) - 1          # indptr[b] <= pos < indptr[b+1]
+            k = round_half_down((pos - indptr[b]) / TILE)
+            bounds[w] = min(indptr[b] + TILE * k, indptr[b + 1])
     per_worker = [[] for _ in range(workers)]
     slot = 0
     for b in range(batch):

@@ -196,10 +196,11 @@ __device__ __forceinline__ void process_segment(
   // buffers: while one tile is computed the other is in flight. Page ids are
   // fetched two tiles ahead and issued before the K/V loads of the tile
   // after the one being computed, so waiting for them never waits for
-  // younger K/V loads. The loop body has no early exit (an odd tile count
-  // ends with one fully masked tile), and the empty asm statements keep every
-  // load group where it is written.
-  const int n_pairs = (n + 2 * kTileTok - 1) / (2 * kTileTok);
+  // younger K/V loads. The loop body has no early exit and the empty asm
+  // statements keep every load group where it is written; an odd last tile is
+  // computed after the loop from the buffer the last pair prefetched into.
+  const int n_tiles = (n + kTileTok - 1) / kTileTok;
+  const int n_pairs = n_tiles / 2;
   int32_t pa0 = ids[min(r, last)];
   int32_t pa1 = ids[min(16 + r, last)];
   int32_t pb0 = ids[min(32 + r, last)];
@@ -226,6 +227,7 @@ __device__ __forceinline__ void process_segment(
     __builtin_amdgcn_sched_barrier(0);
     t0 += 2 * kTileTok;
   }
+  if (n_tiles & 1) compute_tile(ta, t0, n, qf, scale_log2, r, c, lw, st);
 
   float l_tot = st.l + __shfl_xor(st.l, 16);
   l_tot += __shfl_xor(l_tot, 32);
@@ -254,7 +256,7 @@ __device__ __forceinline__ void process_segment(
 }
 
 // One workgroup per worker: it walks its segments in order.
-__global__ __launch_bounds__(kThreads) void decode_partial_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_partial_kernel(
     const int32_t* __restrict__ worker_ptr, const int32_t* __restrict__ segments,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
     const uint16_t* __restrict__ v_pool, const int32_t* __restrict__ kv_indptr,

@@ -59,8 +59,26 @@ bool build_partition(const int32_t* kv_indptr, int32_t batch, int32_t num_cus,
     workers = std::min<int64_t>(int64_t(num_cus) * kWorkersPerCu, cdiv(total, kMinWorkerTokens));
   }
   p.n_workers = static_cast<int32_t>(workers);
-  // Worker w owns the tokens [w*total/workers, (w+1)*total/workers).
-  auto start = [&](int64_t w) { return w * total / workers; };
+  // Worker w owns the tokens [start[w], start[w+1]), start[w] = w*total/workers,
+  // each interior boundary moved (by at most 16 tokens) to the nearest
+  // position that is a multiple of kTile tokens into its sequence, or to the
+  // sequence's end, so that pieces of a sequence are whole tiles. Shares under
+  // kSnapMinShare tokens are not moved.
+  std::vector<int64_t> starts(static_cast<size_t>(workers) + 1);
+  for (int64_t w = 0; w <= workers; ++w) starts[static_cast<size_t>(w)] = workers ? w * total / workers : 0;
+  if (workers > 1 && total / workers >= kSnapMinShare) {
+    for (int64_t w = 1; w < workers; ++w) {
+      const int64_t pos = starts[static_cast<size_t>(w)];
+      // sequence holding pos: last b with kv_indptr[b] <= pos
+      const int32_t b = static_cast<int32_t>(
+          std::upper_bound(kv_indptr, kv_indptr + batch + 1, static_cast<int32_t>(pos)) - kv_indptr - 1);
+      const int64_t off = pos - kv_indptr[b];
+      int64_t snapped = kv_indptr[b] + kTile * ((off + kTile / 2 - 1) / kTile);
+      snapped = std::min<int64_t>(snapped, kv_indptr[b + 1]);
+      starts[static_cast<size_t>(w)] = snapped;
+    }
+  }
+  auto start = [&](int64_t w) { return starts[static_cast<size_t>(w)]; };
 
   std::vector<std::vector<Segment>> per_worker(static_cast<size_t>(workers));
   int32_t slot = 0;

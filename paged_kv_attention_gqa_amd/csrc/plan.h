@@ -1,7 +1,8 @@
 // Split-KV work partition for paged decode (host only, no HIP).
 //
 // The batch's tokens, taken in kv_indices order, are cut into equal
-// contiguous ranges, one per worker (one workgroup of the decode kernel).
+// contiguous ranges, one per worker (one workgroup of the decode kernel); each
+// cut inside a sequence is moved to a whole number of 32-token tiles into it.
 // A worker's range is a list of segments (b, tok_begin, tok_end, slot), one
 // per sequence it touches, with token positions relative to the sequence. A
 // sequence that lies inside one worker is written directly (slot = -1); a
@@ -23,6 +24,8 @@ namespace pkv {
 
 constexpr int32_t kWorkersPerCu = 2;       // decode workgroups resident per CU
 constexpr int32_t kMinWorkerTokens = 128;  // fewest tokens given to one worker
+constexpr int32_t kTile = 32;              // tokens per decode tile
+constexpr int32_t kSnapMinShare = 64;      // shares at least this long get tile-aligned boundaries
 
 struct Segment {
   int32_t b, tok_begin, tok_end, slot;

@@ -38,7 +38,13 @@ def _check(indptr, num_cus, allow_split, chunk_tokens):
     assert [m[0] for m in merges] == sorted(m[0] for m in merges)
     if allow_split and total:
         sizes = [sum(hi - lo for _, lo, hi, _ in segs) for segs in per_worker]
-        assert max(sizes) - min(sizes) <= 1                   # equal shares
+        snapped = len(per_worker) > 1 and total // len(per_worker) >= plan_ref.SNAP_MIN_SHARE
+        assert max(sizes) - min(sizes) <= (1 + 4 * (plan_ref.TILE // 2) if snapped else 1)
+        if snapped:   # interior pieces of a sequence are whole tiles
+            for segs in per_worker:
+                for b, lo, hi, slot in segs:
+                    if slot >= 0 and hi < int(indptr[b + 1] - indptr[b]):
+                        assert (hi - lo) % plan_ref.TILE == 0 or lo % plan_ref.TILE != 0
         if chunk_tokens == 0:
             assert len(per_worker) <= num_cus * plan_ref.WORKERS_PER_CU
     if not allow_split:
@@ -63,15 +69,23 @@ def test_plan_no_split_is_one_worker_per_sequence():
 
 
 def test_plan_hand_example():
-    # 610 tokens over ceil(610/256) = 3 workers: [0,203), [203,406), [406,610)
+    # 610 tokens over ceil(610/256) = 3 workers: cuts at 203 and 406, moved to
+    # the nearest multiple of 32 into sequence 0: 192 (203 = 6*32 + 11) and 416
     per_worker, merges, slots = plan_ref.make_plan([0, 600, 600, 610], 1, chunk_tokens=256)
-    assert per_worker == [[(0, 0, 203, 0)], [(0, 203, 406, 1)], [(0, 406, 600, 2), (2, 0, 10, -1)]]
+    assert per_worker == [[(0, 0, 192, 0)], [(0, 192, 416, 1)], [(0, 416, 600, 2), (2, 0, 10, -1)]]
     assert merges == [(0, 0, 3, 0), (1, 0, 0, 0)] and slots == 3
     assert plan_ref.export([0, 600, 600, 610], 1, chunk_tokens=256) == (
-        [3, 4, 2, 3, 0, 1, 2, 4, 0, 0, 203, 0, 0, 203, 406, 1, 0, 406, 600, 2, 2, 0, 10, -1,
+        [3, 4, 2, 3, 0, 1, 2, 4, 0, 0, 192, 0, 0, 192, 416, 1, 0, 416, 600, 2, 2, 0, 10, -1,
          0, 0, 3, 0, 1, 0, 0, 0])
 
 
-def test_plan_small_batch_uses_few_workers():
-    per_worker, merges, slots = plan_ref.make_plan([0, 17, 81], 256)
-    assert per_worker == [[(0, 0, 17, -1), (1, 0, 64, -1)]] and merges == [] and slots == 0
+def test_plan_snap_ties_and_sequence_end():
+    # a cut at 80 = 2.5 tiles into the sequence (a tie) goes down to 64
+    pw, _, _ = plan_ref.make_plan([0, 160], 1, chunk_tokens=80)
+    assert [s[:3] for ws in pw for s in ws] == [(0, 0, 64), (0, 64, 160)]
+    # a cut at 115 (3.6 tiles into a 120-token sequence) stops at its end
+    pw, _, _ = plan_ref.make_plan([0, 120, 230], 1, chunk_tokens=115)
+    assert pw == [[(0, 0, 120, -1)], [(1, 0, 110, -1)]]
+    # shares under SNAP_MIN_SHARE are not moved
+    pw, _, _ = plan_ref.make_plan([0, 96], 1, chunk_tokens=48)
+    assert [s[:3] for ws in pw for s in ws] == [(0, 0, 48), (0, 48, 96)]

@@ -21,6 +21,7 @@ __all__ = [
     "PkvError", "Plan", "decode", "gather_mla", "library_path",
     "pkv_workspace_size", "pkv_plan_create", "pkv_plan_destroy", "pkv_plan_export",
     "pkv_run", "pkv_merge", "pkv_gather_mla_workspace_size", "pkv_gather_mla",
+    "prepare_run", "prepare_merge",
     "pkv_status_string", "pkv_last_error",
 ]
 
@@ -201,8 +202,8 @@ def pkv_plan_export(plan: Plan) -> list:
     return list(buf)
 
 
-def pkv_run(plan: Plan, q, k_pool, v_pool, kv_indptr, kv_indices, sm_scale, workspace, out,
-            lse, stream=None):
+def _run_args(plan: Plan, q, k_pool, v_pool, kv_indptr, kv_indices, sm_scale, workspace, out,
+              lse, stream):
     import torch
     bf = _bf16_types()
     _require(q, "q", bf)
@@ -219,12 +220,46 @@ def pkv_run(plan: Plan, q, k_pool, v_pool, kv_indptr, kv_indices, sm_scale, work
         raise ValueError("k_pool and v_pool must have the same shape")
     if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != tuple(q.shape[:2]):
         raise ValueError("out must be shaped like q and lse like q.shape[:2]")
-    _check(lib().pkv_run(plan.handle, _ptr(q), q.shape[0], q.shape[1], q.shape[2], _ptr(k_pool),
-                         _ptr(v_pool), k_pool.shape[0], k_pool.shape[1], k_pool.shape[2],
-                         k_pool.shape[3], _ptr(kv_indptr), kv_indptr.numel(), _ptr(kv_indices),
-                         kv_indices.numel(), float(sm_scale), _ptr(workspace), workspace.numel(),
-                         _ptr(out), _ptr(lse), _stream(stream)),
+    return (plan.handle, _ptr(q), q.shape[0], q.shape[1], q.shape[2], _ptr(k_pool), _ptr(v_pool),
+            k_pool.shape[0], k_pool.shape[1], k_pool.shape[2], k_pool.shape[3], _ptr(kv_indptr),
+            kv_indptr.numel(), _ptr(kv_indices), kv_indices.numel(), float(sm_scale),
+            _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse), _stream(stream))
+
+
+def pkv_run(plan: Plan, q, k_pool, v_pool, kv_indptr, kv_indices, sm_scale, workspace, out,
+            lse, stream=None):
+    _check(lib().pkv_run(*_run_args(plan, q, k_pool, v_pool, kv_indptr, kv_indices, sm_scale,
+                                    workspace, out, lse, stream)),
            "pkv_run")
+
+
+def prepare_run(plan: Plan, q, k_pool, v_pool, kv_indptr, kv_indices, sm_scale, workspace, out,
+                lse, stream=None):
+    """Marshal the arguments of pkv_run once; the returned callable enqueues the
+    same call again (same tensors, same stream) with no per-call checks in Python.
+    The tensors must stay alive and in place while the callable is used."""
+    args = _run_args(plan, q, k_pool, v_pool, kv_indptr, kv_indices, sm_scale, workspace, out,
+                     lse, stream)
+    fn = plan._lib.pkv_run
+
+    def call():
+        st = fn(*args)
+        if st != PKV_OK:
+            _check(st, "pkv_run")
+    return call
+
+
+def prepare_merge(plan: Plan, workspace, out, lse, stream=None):
+    """Like prepare_run, for pkv_merge."""
+    args = (plan.handle, _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse),
+            _stream(stream))
+    fn = plan._lib.pkv_merge
+
+    def call():
+        st = fn(*args)
+        if st != PKV_OK:
+            _check(st, "pkv_merge")
+    return call
 
 
 def pkv_merge(plan: Plan, workspace, out, lse, stream=None):

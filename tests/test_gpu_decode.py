@@ -172,3 +172,21 @@ def test_plan_mismatch_raises():
         pkv.pkv_run(plan, dev["q"][:1].contiguous(), dev["k"], dev["v"], dev["indptr"][:2].contiguous(),
                     dev["indices"][:17].contiguous(), w.sm_scale, ws, out[:1].contiguous(),
                     lse[:1].contiguous())
+
+
+def test_prepared_calls_match():
+    """prepare_run / prepare_merge enqueue the same call as pkv_run / pkv_merge."""
+    w = workload("edge")
+    dev = upload_gqa(w)
+    ws = torch.empty(pkv.pkv_workspace_size(w.kv_indptr), dtype=torch.uint8, device="cuda")
+    plan = pkv.pkv_plan_create(w.kv_indptr, workspace=ws)
+    out = torch.empty_like(dev["q"])
+    lse = torch.empty(dev["q"].shape[:2], dtype=torch.float32, device="cuda")
+    run = pkv.prepare_run(plan, dev["q"], dev["k"], dev["v"], dev["indptr"], dev["indices"],
+                          w.sm_scale, ws, out, lse)
+    merge = pkv.prepare_merge(plan, ws, out, lse)
+    for _ in range(2):
+        run()
+        merge()
+    torch.cuda.synchronize()
+    check(w, oracle("edge"), (bf16_to_np(out), lse.cpu().numpy().astype(np.float64)), "prepared")

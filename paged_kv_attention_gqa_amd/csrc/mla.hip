@@ -9,8 +9,14 @@
 //
 // Design:
 // * Work is split three ways: row b, a block of up to 64 query heads, and a
-//   contiguous piece of the index list; one workgroup (4 waves) per triple,
-//   wave w owning 16 heads. Pieces of one (row, head block) leave normalised
+//   contiguous piece of the index list; one workgroup of 8 waves per triple.
+//   Wave w owns 16 heads (w % 4) and one half (w / 4) of both contractions:
+//   dims [288 half, +288) of the 576-dim scores and dims [256 half, +256) of
+//   the 512-dim output. The two waves of a head group swap their partial
+//   scores through LDS, so both hold the full scores, run the same softmax,
+//   and each accumulates its half of the output: no MFMA work is repeated and
+//   each wave keeps 36 registers of Q and 64 of accumulators, which lets two
+//   waves share each SIMD. Pieces of one (row, head block) leave normalised
 //   fp32 partials that a second kernel merges by LSE (vLLM fork qsa.py,
 //   _qsa_merge_splitk_kernel); with a single piece the output is final.
 // * 128 heads share every gathered row, so both contractions are dense and
@@ -20,11 +26,11 @@
 //   The transposing LDS read hands each lane four tokens of one dim, so V is
 //   never rewritten transposed. The S^T accumulator already holds each lane's
 //   P^T operand (head = lane % 16, tokens 16h + 4c + j), as in the GQA kernel.
-// * A tile is 32 gathered rows (36 KB): eight threads per row load it with
-//   16-byte loads (eight lanes cover 128 contiguous bytes) into registers one
-//   tile ahead of the compute (list entries two tiles ahead), then store it to
-//   one of two LDS buffers whose rows are padded to 1168 bytes, conflict-free
-//   for both LDS read patterns.
+// * A tile is 32 gathered rows (36 KB): sixteen threads per row load it with
+//   16-byte loads (consecutive lanes on consecutive bytes) into registers one
+//   two tiles ahead of the compute (list entries three tiles ahead), then
+//   store it to one of two LDS buffers whose rows are padded to 1184 bytes
+//   (the padding measured fastest among 1168-1280 bytes).
 // * A masked entry loads row 0 (so the data is finite) and gets score -inf.
 //   A piece with no valid entry gives out 0 and lse -inf.
 #include <hip/hip_runtime.h>
@@ -42,16 +48,14 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTileTok = 32;
 constexpr int kUnitsPerRow = kMlaDqk / 8;          // 72 units of 16 bytes
-constexpr int kRowU16 = kMlaDqk + 8;               // LDS row: 1152 B + 16 B pad
+constexpr int kRowU16 = kMlaDqk + 16;              // LDS row: 1152 B + 32 B pad
 constexpr int kBufU16 = kTileTok * kRowU16;        // one tile buffer
-constexpr int kThreads = 256;
-constexpr int kLoadsPerThread = kTileTok * kUnitsPerRow / kThreads;   // 9
+constexpr int kThreads = 512;                      // 8 waves
 constexpr int kHeadsPerWave = 16;
 constexpr int kHeadBlock = 4 * kHeadsPerWave;      // 64 heads per workgroup
-constexpr int kQSteps = kMlaDqk / 32;              // 18 k-steps of 32 dims
-constexpr int kVBlocks = kMlaDv / 16;              // 32 blocks of 16 dims
+constexpr int kQSteps = kMlaDqk / 32 / 2;          // 9 k-steps of 32 dims per half
+constexpr int kVBlocks = kMlaDv / 16 / 2;          // 16 blocks of 16 dims per half
 constexpr float kNegInf = -__builtin_huge_valf();
-static_assert(kTileTok * kUnitsPerRow % kThreads == 0, "tile must split evenly");
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
@@ -59,10 +63,11 @@ __device__ __forceinline__ uint16_t bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
-// Thread t stages tile row t / 8: 16-byte units (t % 8) + 8 u, u = 0..8, so
-// eight consecutive lanes read 128 contiguous bytes of one row and every
-// thread needs a single list entry per tile.
-constexpr int kThreadsPerRow = kThreads / kTileTok;   // 8
+// Thread t stages tile row t / 16: 16-byte units (t % 16) + 16 u, u = 0..4
+// (the last only for t % 16 < 8), so sixteen consecutive lanes read 256
+// contiguous bytes of one row and every thread needs one list entry per tile.
+constexpr int kThreadsPerRow = kThreads / kTileTok;   // 16
+constexpr int kLoadsPerThread = (kUnitsPerRow + kThreadsPerRow - 1) / kThreadsPerRow;   // 5
 
 struct Staged {
   u32x4 v[kLoadsPerThread];
@@ -75,6 +80,10 @@ __device__ __forceinline__ int32_t tile_entry(const int32_t* __restrict__ idx, i
   return tok < n ? idx[tok] : -1;
 }
 
+__device__ __forceinline__ bool has_unit(int u) {
+  return u * kThreadsPerRow + static_cast<int>(threadIdx.x % kThreadsPerRow) < kUnitsPerRow;
+}
+
 __device__ __forceinline__ void load_tile(Staged& s, int32_t id, int64_t pool_tokens,
                                           const uint16_t* __restrict__ kv) {
   s.valid = id >= 0 && static_cast<int64_t>(id) < pool_tokens;
@@ -82,7 +91,7 @@ __device__ __forceinline__ void load_tile(Staged& s, int32_t id, int64_t pool_to
                         (threadIdx.x % kThreadsPerRow) * 8;
 #pragma unroll
   for (int u = 0; u < kLoadsPerThread; ++u)
-    s.v[u] = *reinterpret_cast<const u32x4*>(src + u * kThreadsPerRow * 8);
+    if (has_unit(u)) s.v[u] = *reinterpret_cast<const u32x4*>(src + u * kThreadsPerRow * 8);
 }
 
 __device__ __forceinline__ void store_tile(const Staged& s, uint16_t* buf, uint8_t* vflag) {
@@ -90,37 +99,45 @@ __device__ __forceinline__ void store_tile(const Staged& s, uint16_t* buf, uint8
   uint16_t* dst = buf + row * kRowU16 + (threadIdx.x % kThreadsPerRow) * 8;
 #pragma unroll
   for (int u = 0; u < kLoadsPerThread; ++u)
-    *reinterpret_cast<u32x4*>(dst + u * kThreadsPerRow * 8) = s.v[u];
+    if (has_unit(u)) *reinterpret_cast<u32x4*>(dst + u * kThreadsPerRow * 8) = s.v[u];
   if (threadIdx.x % kThreadsPerRow == 0) vflag[row] = s.valid ? 1 : 0;
 }
 
 struct State {
-  f32x4 acc[kVBlocks];   // acc[db][i] = O[head r][16 db + 4c + i]
+  f32x4 acc[kVBlocks];   // acc[db][i] = O[head r][256 half + 16 db + 4c + i]
   float m;               // running max (log2 domain), equal on the 4 lane rows
   float l;               // this lane's share of the exp-sum
 };
 
-__device__ __forceinline__ void compute_tile(const uint16_t* buf, const uint8_t* vflag,
-                                             const u32x4 (&qf)[kQSteps], float scale_log2,
-                                             int r, int c, State& st) {
-  // Four independent accumulator chains (rows 0-15 / 16-31, even / odd k-steps)
-  // keep consecutive MFMAs from waiting on each other.
-  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s0b = s0, s1 = s0, s1b = s0;
-  const uint16_t* row0 = buf + r * kRowU16 + 8 * c;
-  const uint16_t* row1 = buf + (16 + r) * kRowU16 + 8 * c;
+// This wave's half of the scores of one tile: S^T over dims [288 half, +288).
+__device__ __forceinline__ void half_scores(const uint16_t* buf, const u32x4 (&qf)[kQSteps],
+                                            int half, int r, int c, f32x4& s0, f32x4& s1) {
+  // Four accumulator chains (rows 0-15 / 16-31, even / odd k-steps) keep
+  // consecutive MFMAs from waiting on each other.
+  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, b0 = a0, b1 = a0;
+  const uint16_t* row0 = buf + r * kRowU16 + 8 * c + 288 * half;
+  const uint16_t* row1 = row0 + 16 * kRowU16;
 #pragma unroll
-  for (int ks = 0; ks < kQSteps; ks += 2) {
+  for (int ks = 0; ks < kQSteps; ++ks) {
     const u32x4 k0 = *reinterpret_cast<const u32x4*>(row0 + 32 * ks);
     const u32x4 k1 = *reinterpret_cast<const u32x4*>(row1 + 32 * ks);
-    const u32x4 k2 = *reinterpret_cast<const u32x4*>(row0 + 32 * ks + 32);
-    const u32x4 k3 = *reinterpret_cast<const u32x4*>(row1 + 32 * ks + 32);
-    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k0), as_bf16x8(qf[ks]), s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k1), as_bf16x8(qf[ks]), s1, 0, 0, 0);
-    s0b = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k2), as_bf16x8(qf[ks + 1]), s0b, 0, 0, 0);
-    s1b = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k3), as_bf16x8(qf[ks + 1]), s1b, 0, 0, 0);
+    if (ks & 1) {
+      b0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k0), as_bf16x8(qf[ks]), b0, 0, 0, 0);
+      b1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k1), as_bf16x8(qf[ks]), b1, 0, 0, 0);
+    } else {
+      a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k0), as_bf16x8(qf[ks]), a0, 0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k1), as_bf16x8(qf[ks]), a1, 0, 0, 0);
+    }
   }
-  s0 += s0b;
-  s1 += s1b;
+  s0 = a0 + b0;
+  s1 = a1 + b1;
+}
+
+// Online-softmax update with the full scores s0/s1 (identical in both waves of
+// a head group, since a + b == b + a exactly), then this wave's half of P.V.
+__device__ __forceinline__ void softmax_pv(const uint16_t* buf, const uint8_t* vflag, f32x4 s0,
+                                           f32x4 s1, float scale_log2, int half, int r, int c,
+                                           State& st) {
   // p[4h + j] belongs to tile row 16h + 4c + j.
   float p[8];
   float mx = kNegInf;
@@ -151,11 +168,11 @@ __device__ __forceinline__ void compute_tile(const uint16_t* buf, const uint8_t*
 #pragma unroll
   for (int j = 0; j < 8; ++j) pb[j] = static_cast<__bf16>(p[j]);
 
-  // V^T operand: lane (r, c) needs dim 16 db + r of tile rows 16h + 4c + j.
-  // Within each 16-lane group the transposing read gives lane i element i%4
-  // of the 8-byte chunks addressed by lanes 4j + i/4, so lane (r, c) points at
-  // row 16h + 4c + r/4, dims 16 db + 4 (r%4) .. +4.
-  const uint16_t* vrow0 = buf + (4 * c + (r >> 2)) * kRowU16 + 4 * (r & 3);
+  // V^T operand: lane (r, c) needs dim 256 half + 16 db + r of tile rows
+  // 16h + 4c + j. Within each 16-lane group the transposing read gives lane i
+  // element i%4 of the 8-byte chunks addressed by lanes 4j + i/4, so lane
+  // (r, c) points at row 16h + 4c + r/4, dims 256 half + 16 db + 4 (r%4) .. +4.
+  const uint16_t* vrow0 = buf + (4 * c + (r >> 2)) * kRowU16 + 4 * (r & 3) + 256 * half;
   const uint16_t* vrow1 = vrow0 + 16 * kRowU16;
 #pragma unroll
   for (int db = 0; db < kVBlocks; ++db) {
@@ -178,23 +195,29 @@ __global__ __launch_bounds__(kThreads) void mla_partial_kernel(
     float* __restrict__ part_o, float* __restrict__ part_lse) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kBufU16];
   __shared__ uint8_t vflag[2][kTileTok];
+  __shared__ f32x4 xscore[8][2][64];   // each wave's half scores, [wave][mb][lane]
   const int piece = blockIdx.x;
   const int hb = blockIdx.y;
   const int b = blockIdx.z;
   const int pieces = gridDim.x;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
+  const int hg = w & 3;          // head group
+  const int half = w >> 2;       // which half of both contractions
+  const int partner = w ^ 4;
   const int r = lane & 15;
   const int c = lane >> 4;
-  const int head = hb * kHeadBlock + w * kHeadsPerWave + r;
+  const int head = hb * kHeadBlock + hg * kHeadsPerWave + r;
   const bool head_ok = head < num_qo_heads;
+  const bool group_ok = hb * kHeadBlock + hg * kHeadsPerWave < num_qo_heads;
   const int t_begin = piece * per_piece;
   const int n = min(per_piece, topk - t_begin);   // entries of this piece (may be <= 0)
   const int32_t* idx = indices + static_cast<int64_t>(b) * topk + t_begin;
 
   u32x4 qf[kQSteps];
   {
-    const uint16_t* qh = q + (static_cast<int64_t>(b) * num_qo_heads + (head_ok ? head : 0)) * kMlaDqk + 8 * c;
+    const uint16_t* qh = q + (static_cast<int64_t>(b) * num_qo_heads + (head_ok ? head : 0)) * kMlaDqk +
+                         288 * half + 8 * c;
 #pragma unroll
     for (int ks = 0; ks < kQSteps; ++ks)
       qf[ks] = head_ok ? *reinterpret_cast<const u32x4*>(qh + 32 * ks) : u32x4{0u, 0u, 0u, 0u};
@@ -205,23 +228,38 @@ __global__ __launch_bounds__(kThreads) void mla_partial_kernel(
   st.m = kNegInf;
   st.l = 0.f;
 
-  // Pipeline: list entries two tiles ahead, row data one tile ahead.
+  // Pipeline: row data two tiles ahead in two register sets, list entries
+  // three tiles ahead. Loads past the end are issued anyway (entry -1: row 0,
+  // masked) so that every load is unconditional.
   const int n_tiles = n > 0 ? (n + kTileTok - 1) / kTileTok : 0;
-  Staged s;
-  int32_t id_next = 0;
-  if (n_tiles > 0) {
-    load_tile(s, tile_entry(idx, 0, n), pool_tokens, kv);
-    id_next = tile_entry(idx, kTileTok, n);
-  }
-  for (int t = 0; t < n_tiles; ++t) {
-    uint16_t* buf = lds + (t & 1) * kBufU16;
-    const int32_t id_after = tile_entry(idx, (t + 2) * kTileTok, n);
-    store_tile(s, buf, vflag[t & 1]);
-    if (t + 1 < n_tiles) load_tile(s, id_next, pool_tokens, kv);
-    id_next = id_after;
-    __syncthreads();   // tile t is in LDS; every wave is done with tile t-1's buffer
-    if (hb * kHeadBlock + w * kHeadsPerWave < num_qo_heads)
-      compute_tile(buf, vflag[t & 1], qf, scale_log2, r, c, st);
+  Staged sa, sb;
+  load_tile(sa, tile_entry(idx, 0, n), pool_tokens, kv);
+  load_tile(sb, tile_entry(idx, kTileTok, n), pool_tokens, kv);
+  int32_t id_next = tile_entry(idx, 2 * kTileTok, n);
+  for (int t = 0; t < n_tiles; t += 2) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      if (k == 1 && t + 1 >= n_tiles) break;
+      Staged& cur = k == 0 ? sa : sb;
+      uint16_t* buf = lds + k * kBufU16;
+      const int32_t id_after = tile_entry(idx, (t + k + 3) * kTileTok, n);
+      store_tile(cur, buf, vflag[k]);
+      load_tile(cur, id_next, pool_tokens, kv);   // tile t + k + 2
+      id_next = id_after;
+      __syncthreads();   // tile t+k is in LDS; every wave is done with this buffer's last tile
+      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
+      if (group_ok) {
+        half_scores(buf, qf, half, r, c, s0, s1);
+        xscore[w][0][lane] = s0;
+        xscore[w][1][lane] = s1;
+      }
+      __syncthreads();   // both halves of every head group's scores are in LDS
+      if (group_ok) {
+        s0 += xscore[partner][0][lane];
+        s1 += xscore[partner][1][lane];
+        softmax_pv(buf, vflag[k], s0, s1, scale_log2, half, r, c, st);
+      }
+    }
   }
 
   float l_tot = st.l + __shfl_xor(st.l, 16);
@@ -231,7 +269,7 @@ __global__ __launch_bounds__(kThreads) void mla_partial_kernel(
   const float lse2 = any ? st.m + __log2f(l_tot) : kNegInf;
   if (!head_ok) return;
   if (pieces == 1) {
-    uint16_t* o = out + (static_cast<int64_t>(b) * num_qo_heads + head) * kMlaDv + 4 * c;
+    uint16_t* o = out + (static_cast<int64_t>(b) * num_qo_heads + head) * kMlaDv + 256 * half + 4 * c;
 #pragma unroll
     for (int db = 0; db < kVBlocks; ++db) {
       const f32x4 v = st.acc[db] * inv;
@@ -239,13 +277,13 @@ __global__ __launch_bounds__(kThreads) void mla_partial_kernel(
                          static_cast<uint32_t>(bf16_bits(v[2])) | (static_cast<uint32_t>(bf16_bits(v[3])) << 16)};
       *reinterpret_cast<u32x2*>(o + 16 * db) = wds;
     }
-    if (c == 0) lse[static_cast<int64_t>(b) * num_qo_heads + head] = lse2;
+    if (c == 0 && half == 0) lse[static_cast<int64_t>(b) * num_qo_heads + head] = lse2;
   } else {
     const int64_t slot = (static_cast<int64_t>(b) * num_qo_heads + head) * pieces + piece;
-    float* o = part_o + slot * kMlaDv + 4 * c;
+    float* o = part_o + slot * kMlaDv + 256 * half + 4 * c;
 #pragma unroll
     for (int db = 0; db < kVBlocks; ++db) *reinterpret_cast<f32x4*>(o + 16 * db) = st.acc[db] * inv;
-    if (c == 0) part_lse[slot] = lse2;
+    if (c == 0 && half == 0) part_lse[slot] = lse2;
   }
 }
 

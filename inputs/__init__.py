@@ -7,9 +7,11 @@ and the CPU oracle read the same arrays from here.
 
 from .configs import (  # noqa: F401
     CONFIG_NAMES,
+    BlockTableWorkload,
     GqaWorkload,
     MlaWorkload,
     bf16_bits_from_f32,
+    make_block_table,
     make_config,
     make_gqa,
     make_mla,

@@ -8,10 +8,17 @@ Recipe (stated once, used by the tests, the bench and the oracle's pins):
 * Draw order is fixed: sequence lengths, then the physical-page permutation,
   then q, then the K pool, then the V pool, then (index-gather workloads only)
   the index lists.
-* Page size is 1, so a page is one token and ``kv_indptr[b+1] - kv_indptr[b]``
-  is the length of sequence ``b``. Pools are ``[num_pages, 1, H_kv, D]``; the
-  pages of all sequences are a random permutation of the pool, cut in sequence
-  order, so neighbouring tokens of a sequence sit at unrelated addresses.
+* CSR workloads have page size 1, so a page is one token and
+  ``kv_indptr[b+1] - kv_indptr[b]`` is the length of sequence ``b``. Pools are
+  ``[num_pages, 1, H_kv, D]``; the pages of all sequences are a random
+  permutation of the pool, cut in sequence order, so neighbouring tokens of a
+  sequence sit at unrelated addresses.
+* Block-table workloads have page size ``ps`` > 1 (pools
+  ``[num_pages, ps, H_kv, D]``): sequence ``b`` of length ``n`` owns
+  ``ceil(n / ps)`` pages, taken in sequence order from a random permutation
+  of the pool and listed in row ``b`` of ``block_table``; its last page is
+  partly filled when ``ps`` does not divide ``n``. Entries past a row's pages
+  hold ``pad_value``.
 
 The five named workloads follow the paged GQA decode definition (32 query heads,
 4 KV heads, head_dim 128, page size 1) and the index-gather latent-attention
@@ -28,7 +35,7 @@ from typing import Optional, Sequence
 
 import numpy as np
 
-CONFIG_NAMES = ("tiny", "gqa", "edge", "throughput", "mla")
+CONFIG_NAMES = ("tiny", "gqa", "edge", "throughput", "mla", "gqa_ps16", "gqa_ps64", "edge_ps16")
 
 # Sequence lengths of the edge-case batch: empty, single token, tile edges,
 # a long tail and one 32768-token sequence that holds about half the bytes.
@@ -79,6 +86,47 @@ class GqaWorkload:
     @property
     def lengths(self) -> np.ndarray:
         return np.diff(self.kv_indptr.astype(np.int64))
+
+
+@dataclasses.dataclass
+class BlockTableWorkload:
+    """Inputs of one paged GQA decode call through a block table."""
+
+    name: str
+    seed: int
+    q: np.ndarray            # uint16 bf16 bits [B, Hq, D]
+    k_pool: np.ndarray       # uint16 bf16 bits [P, ps, Hkv, D]
+    v_pool: np.ndarray       # uint16 bf16 bits [P, ps, Hkv, D]
+    block_table: np.ndarray  # int32 [B, max_pages]
+    seq_lens: np.ndarray     # int32 [B]
+    sm_scale: float
+    num_qo_heads: int
+    num_kv_heads: int
+    head_dim: int
+
+    @property
+    def batch(self) -> int:
+        return int(self.seq_lens.shape[0])
+
+    @property
+    def page_size(self) -> int:
+        return int(self.k_pool.shape[1])
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.k_pool.shape[0])
+
+    @property
+    def total_tokens(self) -> int:
+        return int(self.seq_lens.astype(np.int64).sum())
+
+    @property
+    def lengths(self) -> np.ndarray:
+        return self.seq_lens.astype(np.int64)
+
+    @property
+    def pages_per_seq(self) -> np.ndarray:
+        return -(-self.lengths // self.page_size)
 
 
 @dataclasses.dataclass
@@ -171,6 +219,57 @@ def make_gqa(seed: int, lengths: Sequence[int], *, num_qo_heads: int = 32,
                        num_kv_heads=num_kv_heads, head_dim=head_dim)
 
 
+def make_block_table(seed: int, lengths: Sequence[int], page_size: int, *,
+                     num_qo_heads: int = 32, num_kv_heads: int = 4, head_dim: int = 128,
+                     pool_pages: Optional[int] = None, extra_cols: int = 0,
+                     pad_value: int = 0, peaky_seq: Optional[int] = None,
+                     peaky_factor: float = 30.0, const_v_seq: Optional[int] = None,
+                     const_v: float = EDGE_CONST_V, sm_scale: Optional[float] = None,
+                     name: str = "custom",
+                     rng: Optional[np.random.Generator] = None) -> BlockTableWorkload:
+    """Build one paged GQA decode input addressed through a block table.
+
+    ``pool_pages`` defaults to the pages the batch needs; with a larger pool
+    some pages are never referenced. The table has ``max(pages) + extra_cols``
+    columns; unused entries hold ``pad_value``. The peaky / constant-V edits
+    cover every slot of the chosen sequence's pages.
+    """
+    if rng is None:
+        rng = np.random.default_rng(seed)
+    lengths = np.asarray(lengths, dtype=np.int64)
+    batch = int(lengths.shape[0])
+    need = -(-lengths // page_size)
+    total_pages = int(need.sum())
+    pages = total_pages if pool_pages is None else int(pool_pages)
+    if pages < total_pages:
+        raise ValueError("pool smaller than the number of pages the batch needs")
+    perm = rng.permutation(max(pages, 0)).astype(np.int32)
+    cols = int(need.max(initial=0)) + int(extra_cols)
+    table = np.full((batch, cols), pad_value, dtype=np.int32)
+    first = np.concatenate([[0], np.cumsum(need)])
+    for b in range(batch):
+        table[b, :need[b]] = perm[first[b]:first[b + 1]]
+
+    q32 = _draw_bf16(rng, (batch, num_qo_heads, head_dim))
+    k32 = _draw_bf16(rng, (pages, page_size, num_kv_heads, head_dim))
+    if peaky_seq is not None:
+        k32[table[peaky_seq, :need[peaky_seq]]] *= np.float32(peaky_factor)
+    k_bits = bf16_bits_from_f32(k32)
+    del k32
+    v32 = _draw_bf16(rng, (pages, page_size, num_kv_heads, head_dim))
+    if const_v_seq is not None:
+        v32[table[const_v_seq, :need[const_v_seq]]] = np.float32(const_v)
+    v_bits = bf16_bits_from_f32(v32)
+    del v32
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(head_dim)
+    return BlockTableWorkload(name=name, seed=seed, q=bf16_bits_from_f32(q32), k_pool=k_bits,
+                              v_pool=v_bits, block_table=table,
+                              seq_lens=lengths.astype(np.int32), sm_scale=float(sm_scale),
+                              num_qo_heads=num_qo_heads, num_kv_heads=num_kv_heads,
+                              head_dim=head_dim)
+
+
 def make_mla(seed: int, *, batch: int = 32, num_qo_heads: int = 128, d_qk: int = 576,
              d_v: int = 512, pool_tokens: int = 65536, topk: int = 2048,
              masked_per_row: Optional[int] = None, sm_scale: Optional[float] = None,
@@ -200,7 +299,8 @@ def make_mla(seed: int, *, batch: int = 32, num_qo_heads: int = 128, d_qk: int =
 
 
 def make_config(name: str):
-    """The five named workloads (seeds 1..5)."""
+    """The named workloads: five with page size 1 (seeds 1..5) and three
+    block-table workloads with page size 16 or 64 (seeds 6..8)."""
     if name == "tiny":
         return make_gqa(1, [17, 64], pool_pages=128, name="tiny")
     if name == "gqa":
@@ -216,4 +316,12 @@ def make_config(name: str):
         return make_gqa(4, lengths, name="throughput", rng=rng)
     if name == "mla":
         return make_mla(5, name="mla")
+    if name in ("gqa_ps16", "gqa_ps64"):
+        seed, ps = (6, 16) if name == "gqa_ps16" else (7, 64)
+        rng = np.random.default_rng(seed)
+        lengths = rng.integers(512, 4096, size=64, endpoint=True)
+        return make_block_table(seed, lengths, ps, name=name, rng=rng)
+    if name == "edge_ps16":
+        return make_block_table(8, EDGE_LENGTHS, 16, peaky_seq=EDGE_PEAKY_SEQ,
+                                const_v_seq=EDGE_CONST_V_SEQ, name="edge_ps16")
     raise KeyError(name)

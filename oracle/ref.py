@@ -10,7 +10,9 @@ Sources (page title, then the function or step on it):
   the kernel ``gqa_paged_decode_h32_kv4_d128_ps1_kernel`` (its numbered steps
   2, 4, 7, 8 and 9) and its wrapper ``run``.
 * [MLA page] FlagGems docs, coverage page of ``flash_mla_with_kvcache.py``:
-  ``_sparse_decode_kernel`` (index masking, the 576/512 latent split).
+  ``_sparse_decode_kernel`` (index masking, the 576/512 latent split) and
+  ``_dense_decode_kernel`` (pages of several tokens found through a block
+  table, sequence lengths that end inside a page).
 * [QSA page] vLLM fork, ``vllm/models/qwen4_exp/amd/ops/qsa.py``:
   ``_qsa_sparse_paged_gqa_splitk_kernel`` (normalised partials with a base-2
   LSE) and ``_qsa_merge_splitk_kernel`` (the LSE merge).
@@ -116,6 +118,38 @@ def gqa_paged_decode(q_bits, k_bits, v_bits, kv_indptr, kv_indices, sm_scale: fl
         n = int(kv_indptr[b + 1]) - int(kv_indptr[b])
         out[b], lse[b] = gqa_decode_range(q_bits, k_bits, v_bits, kv_indptr, kv_indices,
                                           sm_scale, b, 0, n)
+    return out, lse
+
+
+def gqa_block_table_decode(q_bits, k_bits, v_bits, block_table, seq_lens, sm_scale: float,
+                           batches=None):
+    """Paged GQA decode with pages of several tokens, found through a block table.
+
+    Pools are ``[P, page_size, Hkv, D]``. Sequence ``b`` has ``seq_lens[b]``
+    tokens; its token ``j`` sits in page ``block_table[b, j // page_size]`` at
+    slot ``j % page_size`` ([MLA page] ``_dense_decode_kernel``: the page
+    number from the table, the row inside the page from the remainder, and the
+    tokens past the sequence length masked). Only the first
+    ``ceil(seq_lens[b] / page_size)`` entries of a table row are read, and in
+    the last page only the slots below the length. Per KV head the attention is
+    the same as with single-token pages. Returns ``out [B, Hq, D]`` and
+    ``lse [B, Hq]`` in fp64 (rows not listed in ``batches`` are NaN).
+    """
+    batch, num_qo_heads, _ = q_bits.shape
+    page_size, num_kv_heads = k_bits.shape[1], k_bits.shape[2]
+    out = np.full((batch, num_qo_heads, v_bits.shape[3]), np.nan)
+    lse = np.full((batch, num_qo_heads), np.nan)
+    for b in (range(batch) if batches is None else batches):
+        j = np.arange(int(seq_lens[b]), dtype=np.int64)
+        pages = np.asarray(block_table[b], dtype=np.int64)[j // page_size]
+        slots = j % page_size
+        q = bf16_to_f64(q_bits[b])
+        for g in range(num_kv_heads):
+            heads = [h for h in range(num_qo_heads)
+                     if gqa_group_of(h, num_qo_heads, num_kv_heads) == g]
+            k = bf16_to_f64(k_bits[pages, slots, g, :])          # [n, D]
+            v = bf16_to_f64(v_bits[pages, slots, g, :])
+            out[b, heads], lse[b, heads] = attend(q[heads], k, v, sm_scale)
     return out, lse
 
 

@@ -14,7 +14,7 @@ import math
 import numpy as np
 import torch
 
-from inputs import bf16_bits_from_f32, make_config, make_gqa, make_mla
+from inputs import bf16_bits_from_f32, make_block_table, make_config, make_gqa, make_mla
 from inputs.configs import EDGE_CONST_V, EDGE_CONST_V_SEQ, EDGE_LENGTHS
 
 _CACHE = {}
@@ -381,6 +381,122 @@ def pin_mla_duplicates_count(ref):
     want = (e @ rows[:, :w.d_v]) / e.sum(axis=1, keepdims=True)
     assert np.max(np.abs(out[0] - want)) <= 1e-12
     assert np.max(np.abs(lse[0] - np.log2(e.sum(axis=1)))) <= 1e-12
+
+
+# ------------------------------------------------------ block-table decode
+
+def _small_bt(page_size=16):
+    key = f"small_bt{page_size}"
+    if key not in _CACHE:
+        _CACHE[key] = make_block_table(31 + page_size, [0, 1, 15, 16, 17, 40, 64, 5],
+                                       page_size, extra_cols=3, pool_pages=None)
+    return _CACHE[key]
+
+
+def _bt(ref, w, **kw):
+    return ref.gqa_block_table_decode(w.q, w.k_pool, w.v_pool, w.block_table, w.seq_lens,
+                                      w.sm_scale, **kw)
+
+
+def pin_bt_sdpa(ref):
+    """Against torch SDPA over rows gathered one token at a time from the flat pool."""
+    for ps in (4, 16):
+        w = _small_bt(ps)
+        out, lse = _bt(ref, w)
+        flat_k = torch.as_tensor(_f64(w.k_pool)).reshape(-1, w.num_kv_heads, w.head_dim)
+        flat_v = torch.as_tensor(_f64(w.v_pool)).reshape(-1, w.num_kv_heads, w.head_dim)
+        for b in range(w.batch):
+            n = int(w.seq_lens[b])
+            if n == 0:
+                assert np.all(out[b] == 0.0) and np.all(np.isneginf(lse[b]))
+                continue
+            rows = []
+            for j in range(n):
+                page, slot = divmod(j, ps)
+                rows.append(int(w.block_table[b, page]) * ps + slot)
+            rows = torch.tensor(rows)
+            q = torch.as_tensor(_f64(w.q[b]))[:, None, :]                 # [Hq, 1, D]
+            k = flat_k[rows].transpose(0, 1).contiguous()                  # [Hkv, n, D]
+            v = flat_v[rows].transpose(0, 1).contiguous()
+            o = torch.nn.functional.scaled_dot_product_attention(
+                q[None], k[None], v[None], scale=w.sm_scale, enable_gqa=True)[0, :, 0, :]
+            assert np.max(np.abs(out[b] - o.numpy())) <= 1e-12
+            kk = k.repeat_interleave(w.num_qo_heads // w.num_kv_heads, dim=0)
+            scores = w.sm_scale * torch.bmm(q, kk.transpose(1, 2).contiguous())[:, 0, :]
+            l2 = (torch.logsumexp(scores, dim=-1) / math.log(2.0)).numpy()
+            assert np.max(np.abs(lse[b] - l2)) <= 1e-12
+
+
+def pin_bt_brute_force(ref):
+    """Page size 4, lengths 3 and 9 (a partial page each), summed term by term."""
+    w = make_block_table(41, [3, 9], 4, extra_cols=1)
+    out, lse = _bt(ref, w)
+    for b in range(2):
+        q = _f64(w.q[b])
+        for h in range(0, 32, 3):
+            g = h // 8
+            ks, vs = [], []
+            for j in range(int(w.seq_lens[b])):
+                page = int(w.block_table[b][j // 4])
+                ks.append(_f64(w.k_pool[page, j % 4, g]))
+                vs.append(_f64(w.v_pool[page, j % 4, g]))
+            s = [w.sm_scale * math.fsum(float(a) * float(c) for a, c in zip(q[h], k)) for k in ks]
+            e = [math.exp(x) for x in s]
+            z = math.fsum(e)
+            assert abs(lse[b, h] - math.log2(z)) <= 1e-12 * max(1.0, abs(math.log2(z)))
+            for d in range(0, 128, 5):
+                o = math.fsum(ei * float(vr[d]) for ei, vr in zip(e, vs)) / z
+                assert abs(out[b, h, d] - o) <= 1e-12
+
+
+def pin_bt_reduces_to_single_token_pages(ref):
+    """Split every page into single-token pages and list them through the CSR
+    function: the same rows in the same order give the same result, bit for bit."""
+    for ps in (4, 16):
+        w = _small_bt(ps)
+        out, lse = _bt(ref, w)
+        k1 = w.k_pool.reshape(-1, 1, w.num_kv_heads, w.head_dim)
+        v1 = w.v_pool.reshape(-1, 1, w.num_kv_heads, w.head_dim)
+        idx = []
+        for b in range(w.batch):
+            for j in range(int(w.seq_lens[b])):
+                idx.append(int(w.block_table[b, j // ps]) * ps + j % ps)
+        indptr = np.concatenate([[0], np.cumsum(w.seq_lens)]).astype(np.int32)
+        o1, l1 = ref.gqa_paged_decode(w.q, k1, v1, indptr, np.array(idx, np.int32), w.sm_scale)
+        assert np.array_equal(out, o1) and np.array_equal(lse, l1)
+
+
+def pin_bt_unread_entries_and_slots(ref):
+    """Table entries past a sequence's pages, slots past its length in the last
+    page and pages nobody lists never reach the result."""
+    w = _small_bt(16)
+    out, lse = _bt(ref, w)
+    table = w.block_table.copy()
+    k = w.k_pool.copy()
+    v = w.v_pool.copy()
+    for b in range(w.batch):
+        n = int(w.seq_lens[b])
+        used = -(-n // 16)
+        table[b, used:] = -1
+        if n % 16:
+            k[table[b, used - 1], n % 16:] = 0x7FC0
+            v[table[b, used - 1], n % 16:] = 0x7FC0
+    listed = np.zeros(w.num_pages, dtype=bool)
+    for b in range(w.batch):
+        listed[table[b][table[b] >= 0]] = True
+    k[~listed] = 0x7FC0
+    v[~listed] = 0x7FC0
+    o1, l1 = ref.gqa_block_table_decode(w.q, k, v, table, w.seq_lens, w.sm_scale)
+    assert np.array_equal(out, o1) and np.array_equal(lse, l1)
+
+
+def pin_bt_single_token_and_empty(ref):
+    w = _small_bt(16)
+    out, lse = _bt(ref, w)
+    assert np.all(out[0] == 0.0) and np.all(np.isneginf(lse[0]))
+    page = int(w.block_table[1, 0])
+    for h in range(32):
+        assert np.array_equal(out[1, h], _f64(w.v_pool[page, 0, h // 8]))
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

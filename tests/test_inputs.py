@@ -69,3 +69,25 @@ def test_mla_structure():
         assert int((row == -1).sum()) == 102
         kept = row[row >= 0]
         assert len(np.unique(kept)) == len(kept) and kept.max() < 65536
+
+
+def test_block_table_structure():
+    for name, ps in (("gqa_ps16", 16), ("gqa_ps64", 64), ("edge_ps16", 16)):
+        w = make_config(name)
+        assert w.page_size == ps and w.k_pool.shape[1:] == (ps, 4, 128)
+        need = w.pages_per_seq
+        assert w.block_table.shape == (w.batch, need.max())
+        used = np.concatenate([w.block_table[b, :need[b]] for b in range(w.batch)])
+        assert np.array_equal(np.sort(used), np.arange(w.num_pages))   # each page once
+    w = make_config("edge_ps16")
+    assert tuple(w.lengths) == EDGE_LENGTHS
+    pages = w.block_table[7, :w.pages_per_seq[7]]
+    assert np.all(w.v_pool[pages] == 0x3F40)
+
+
+def test_block_table_padding_and_extra_columns():
+    from inputs import make_block_table
+    w = make_block_table(9, [0, 1, 16, 17], 16, extra_cols=2, pad_value=-1, pool_pages=10)
+    assert list(w.pages_per_seq) == [0, 1, 1, 2]
+    assert w.block_table.shape == (4, 4) and w.num_pages == 10
+    assert np.all(w.block_table[0] == -1) and np.all(w.block_table[3, 2:] == -1)

@@ -38,6 +38,16 @@ MUTANTS = {
     "mla_upper_mask_dropped": ("ids = ids[(ids >= 0) & (ids < pool_tokens)]",
                                "ids = ids[(ids >= 0)]"),
     "mla_v_tail": ("rows[:, :d_v]", "rows[:, -d_v:]"),
+    "bt_page_from_remainder": ("[j // page_size]", "[j % page_size]"),
+    "bt_slot_shifted": ("slots = j % page_size", "slots = (j + 1) % page_size"),
+    "bt_slot_ignored": ("k = bf16_to_f64(k_bits[pages, slots, g, :])",
+                        "k = bf16_to_f64(k_bits[pages, 0, g, :])"),
+    "bt_v_slot_reversed": ("v = bf16_to_f64(v_bits[pages, slots, g, :])",
+                           "v = bf16_to_f64(v_bits[pages, page_size - 1 - slots, g, :])"),
+    "bt_whole_pages": ("j = np.arange(int(seq_lens[b]), dtype=np.int64)",
+                       "j = np.arange(-(-int(seq_lens[b]) // page_size) * page_size, dtype=np.int64)"),
+    "bt_one_short": ("j = np.arange(int(seq_lens[b]), dtype=np.int64)",
+                     "j = np.arange(max(int(seq_lens[b]) - 1, 0), dtype=np.int64)"),
     "scores_transposed_q": ("s = sm_scale * (q @ k.T)", "s = sm_scale * (q[::-1] @ k.T)"),
 }
 

@@ -38,36 +38,54 @@ WORKLOAD_TEXT = {
     "edge": "paged GQA decode, B=16 edge-case seq_lens (0..32768), h_q=32 h_kv=4 d=128 page_size=1",
     "throughput": "paged GQA decode, B=256, seq_lens log-normal (median 1024, sigma 1, clip "
                   "[1,16384]), h_q=32 h_kv=4 d=128 page_size=1, split-KV",
+    "gqa_ps16": "paged GQA decode through a block table, B=64, seq_lens uniform [512,4096], "
+                "h_q=32 h_kv=4 d=128 page_size=16, pool = the pages the batch needs, randomly "
+                "permuted",
+    "gqa_ps64": "paged GQA decode through a block table, B=64, seq_lens uniform [512,4096], "
+                "h_q=32 h_kv=4 d=128 page_size=64, pool = the pages the batch needs, randomly "
+                "permuted",
+    "edge_ps16": "paged GQA decode through a block table, B=16 edge-case seq_lens (0..32768), "
+                 "h_q=32 h_kv=4 d=128 page_size=16",
 }
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partial_gqa_traffic.txt")
 KERNEL_SRC = os.path.join(ROOT, "paged_kv_attention_gqa_amd", "csrc", "decode.hip")
+
+
+def traffic_file(config: str) -> str:
+    return os.path.join(ROOT, "profiles", f"decode_partial_{config}_traffic.txt")
 
 
 def algorithmic_decode_bytes(w, plan_flat) -> int:
     """Bytes the decode kernel must move per launch (each byte once).
 
-    Per token: 2048 B of K/V rows + 4 B page id. Per sequence: 8192 B of q and
-    the 4-byte indptr entry. Per directly written sequence: 8192 B bf16 out +
-    128 B lse. Per split segment: 16384 B fp32 partial + 128 B partial LSE.
-    Plus the plan tables: 4 B per worker offset and 16 B per segment.
+    Per token: 2048 B of K/V rows. Page ids: 4 B per token for a CSR list
+    (plus the 4-byte indptr entry per sequence), 4 B per page for a block
+    table. Per sequence: 8192 B of q. Per directly written sequence: 8192 B
+    bf16 out + 128 B lse. Per split segment: 16384 B fp32 partial + 128 B
+    partial LSE. Plus the plan tables: 4 B per worker offset and 16 B per
+    segment.
     """
     n_workers, n_segs, n_merges, n_slots = plan_flat[:4]
     segs = np.array(plan_flat[5 + n_workers:5 + n_workers + 4 * n_segs],
                     dtype=np.int64).reshape(-1, 4)
     direct = int(np.sum(segs[:, 3] < 0))
     n = w.total_tokens
-    return (2052 * n + 8192 * w.batch + 4 * (w.batch + 1) + direct * (8192 + 128)
+    if hasattr(w, "block_table"):
+        ids = 4 * int(w.pages_per_seq.sum())
+    else:
+        ids = 4 * n + 4 * (w.batch + 1)
+    return (2048 * n + ids + 8192 * w.batch + direct * (8192 + 128)
             + n_slots * (16384 + 128) + 4 * (n_workers + 1) + 16 * n_segs)
 
 
-def read_traffic(kernel_src: str):
-    """HBM bytes per launch from the committed counter summary, or None if the
-    kernel source has changed since the counters were taken."""
+def read_traffic(config: str, kernel_src: str):
+    """HBM bytes per launch from the committed counter summary of this workload,
+    or None if there is none or the kernel source has changed since."""
     import hashlib
-    if not os.path.exists(TRAFFIC_FILE):
+    path = traffic_file(config)
+    if not os.path.exists(path):
         return None
     vals = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             vals[k.strip()] = v.strip()
@@ -91,7 +109,11 @@ def cpu_baseline(w, budget_s: float):
     reps, t_total = 0, 0.0
     while t_total < budget_s and reps < 50:
         t0 = time.perf_counter()
-        ref.gqa_paged_decode(w.q, w.k_pool, w.v_pool, w.kv_indptr, w.kv_indices, w.sm_scale)
+        if hasattr(w, "block_table"):
+            ref.gqa_block_table_decode(w.q, w.k_pool, w.v_pool, w.block_table, w.seq_lens,
+                                       w.sm_scale)
+        else:
+            ref.gqa_paged_decode(w.q, w.k_pool, w.v_pool, w.kv_indptr, w.kv_indices, w.sm_scale)
         t_total += time.perf_counter() - t0
         reps += 1
     per_call = t_total / reps
@@ -215,25 +237,37 @@ def main():
     reps = args.replicas or max(1, min(8, math.ceil(768e6 / max(pool_bytes, 1)) + 1))
     k0, v0 = as_t(w.k_pool), as_t(w.v_pool)
     pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(reps - 1)]
-    indptr = torch.from_numpy(w.kv_indptr).to(dev)
-    indices = torch.from_numpy(w.kv_indices).to(dev)
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+    block_table = hasattr(w, "block_table")
+    split = not args.no_split
 
     t0 = time.perf_counter()
-    ws_bytes = pkv.pkv_workspace_size(w.kv_indptr, allow_split=not args.no_split,
-                                      chunk_tokens=args.chunk)
+    if block_table:
+        ws_bytes = pkv.pkv_block_table_workspace_size(w.seq_lens, page_size=w.page_size,
+                                                      allow_split=split, chunk_tokens=args.chunk)
+    else:
+        ws_bytes = pkv.pkv_workspace_size(w.kv_indptr, allow_split=split, chunk_tokens=args.chunk)
     plan_us = (time.perf_counter() - t0) * 1e6
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-    plan = pkv.pkv_plan_create(w.kv_indptr, allow_split=not args.no_split,
-                               chunk_tokens=args.chunk, workspace=ws)
-    flat = pkv.pkv_plan_export(plan)
-    torch.cuda.synchronize()
-
     # Arguments are marshalled once per pool replica; the timed loop only
     # enqueues (the library checks every argument in C on each call).
-    runs = [pkv.prepare_run(plan, q, k, v, indptr, indices, w.sm_scale, ws, out, lse)
-            for k, v in pools]
+    if block_table:
+        table = torch.from_numpy(w.block_table).to(dev)
+        plan = pkv.pkv_block_table_plan_create(w.seq_lens, page_size=w.page_size,
+                                               allow_split=split, chunk_tokens=args.chunk,
+                                               workspace=ws)
+        runs = [pkv.prepare_block_table_run(plan, q, k, v, table, w.sm_scale, ws, out, lse)
+                for k, v in pools]
+    else:
+        indptr = torch.from_numpy(w.kv_indptr).to(dev)
+        indices = torch.from_numpy(w.kv_indices).to(dev)
+        plan = pkv.pkv_plan_create(w.kv_indptr, allow_split=split, chunk_tokens=args.chunk,
+                                   workspace=ws)
+        runs = [pkv.prepare_run(plan, q, k, v, indptr, indices, w.sm_scale, ws, out, lse)
+                for k, v in pools]
+    flat = pkv.pkv_plan_export(plan)
+    torch.cuda.synchronize()
     merge = pkv.prepare_merge(plan, ws, out, lse)
 
     for i in range(args.warmup):
@@ -277,7 +311,7 @@ def main():
     value = kv_bytes / (wall / args.steps) / 1e9
     alg = algorithmic_decode_bytes(w, flat)
     achieved = alg / decode_s / 1e9
-    traffic = read_traffic(KERNEL_SRC)
+    traffic = read_traffic(args.config, KERNEL_SRC)
 
     rec = {
         "metric": METRIC,
@@ -298,6 +332,7 @@ def main():
         "data": "synthetic (seeded N(0,1) bf16 q/K/V, random page permutation)",
         "config": {"workload": WORKLOAD_TEXT[args.config], "name": args.config,
                    "batch": w.batch, "total_tokens": w.total_tokens,
+                   "page_size": w.page_size,
                    "split": not args.no_split, "workers": flat[0], "segments": flat[1],
                    "merge_records": flat[2], "partial_slots": flat[3], "pool_replicas": reps,
                    "plan_host_us": round(plan_us, 1)},

@@ -23,8 +23,10 @@
  * (vLLM fork qsa.py, _qsa_sparse_paged_gqa_splitk_kernel and
  * _qsa_merge_splitk_kernel).
  *
- * Supported shapes (compiled in): Hq = 32, Hkv = 4, head_dim = 128,
- * page_size = 1, bf16 q/K/V. Other shapes return PKV_ERR_UNSUPPORTED.
+ * Supported shapes (compiled in): Hq = 32, Hkv = 4, head_dim = 128, bf16
+ * q/K/V; page_size = 1 for the CSR page list (pkv_run) and a power of two up
+ * to 1024 for block tables (pkv_block_table_run). Other shapes return
+ * PKV_ERR_UNSUPPORTED.
  *
  * Layouts (all contiguous, row-major; bf16 as 16-bit patterns; device
  * pointers 16-byte aligned):
@@ -125,6 +127,49 @@ pkv_status pkv_run(const pkv_plan* plan,
                    const int32_t* kv_indices, int64_t num_indices,
                    float sm_scale, void* workspace, size_t workspace_bytes,
                    void* out, float* lse, void* stream);
+
+/*
+ * Paged decode with pages of several tokens found through a block table
+ * (FlagGems flash_mla_with_kvcache page, _dense_decode_kernel: the page from
+ * the table, the slot from the remainder, tokens past the sequence length
+ * masked). Sequence b has seq_lens[b] tokens; its token j is slot
+ * j % page_size of page block_table[b, j / page_size], so the last page may be
+ * partly filled. The attention itself is the one stated at the top of this
+ * file.
+ *
+ * pkv_block_table_workspace_size / pkv_block_table_plan_create take the host
+ * int32 sequence lengths seq_lens_host [batch] (each >= 0, sum < 2^31) in
+ * place of kv_indptr_host; every other argument means what it means for
+ * pkv_workspace_size / pkv_plan_create. The plan fixes the lengths: the
+ * device never reads them, so a plan is made per batch of lengths.
+ *
+ * pkv_block_table_run enqueues the partial decode for such a plan (pkv_run
+ * rejects it with PKV_ERR_PLAN_MISMATCH, and this call rejects a CSR plan).
+ * block_table: device int32 [table_rows, table_cols], row-major; table_rows
+ * must equal the batch and table_cols must be at least the most pages any
+ * sequence needs, ceil(seq_lens[b] / page_size). Only the first
+ * ceil(seq_lens[b] / page_size) entries of row b are read, and each must be a
+ * page in [0, num_pages) (caller precondition, not checked on device); other
+ * entries may hold anything. The pool [num_pages, page_size, Hkv, D] may hold
+ * at most 2^31 - 1 token rows. Finish with pkv_merge as after pkv_run.
+ */
+pkv_status pkv_block_table_workspace_size(const int32_t* seq_lens_host, int32_t batch,
+                                          int32_t num_qo_heads, int32_t num_kv_heads,
+                                          int32_t head_dim, int32_t page_size, int32_t num_cus,
+                                          int32_t allow_split, int32_t chunk_tokens,
+                                          size_t* bytes);
+pkv_status pkv_block_table_plan_create(const int32_t* seq_lens_host, int32_t batch,
+                                       int32_t num_qo_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t page_size, int32_t num_cus,
+                                       int32_t allow_split, int32_t chunk_tokens, void* workspace,
+                                       size_t workspace_bytes, void* stream, pkv_plan** plan);
+pkv_status pkv_block_table_run(const pkv_plan* plan,
+                               const void* q, int32_t q_batch, int32_t q_heads, int32_t q_dim,
+                               const void* k_pool, const void* v_pool, int64_t num_pages,
+                               int32_t page_size, int32_t pool_kv_heads, int32_t pool_dim,
+                               const int32_t* block_table, int32_t table_rows,
+                               int32_t table_cols, float sm_scale, void* workspace,
+                               size_t workspace_bytes, void* out, float* lse, void* stream);
 
 /*
  * Enqueue the LSE merge of the sequences the plan split (and the zero output

@@ -22,6 +22,8 @@ __all__ = [
     "pkv_workspace_size", "pkv_plan_create", "pkv_plan_destroy", "pkv_plan_export",
     "pkv_run", "pkv_merge", "pkv_gather_mla_workspace_size", "pkv_gather_mla",
     "prepare_run", "prepare_merge",
+    "pkv_block_table_workspace_size", "pkv_block_table_plan_create", "pkv_block_table_run",
+    "prepare_block_table_run", "decode_block_table",
     "pkv_status_string", "pkv_last_error",
 ]
 
@@ -48,6 +50,12 @@ SIGNATURES = {
     "pkv_plan_export": (_I32, [_P, _I32P, _SZ, _c.POINTER(_SZ)]),
     "pkv_run": (_I32, [_P, _P, _I32, _I32, _I32, _P, _P, _I64, _I32, _I32, _I32, _P, _I64, _P,
                        _I64, _c.c_float, _P, _SZ, _P, _P, _P]),
+    "pkv_block_table_workspace_size": (_I32, [_I32P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                              _I32, _c.POINTER(_SZ)]),
+    "pkv_block_table_plan_create": (_I32, [_I32P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                           _I32, _P, _SZ, _P, _c.POINTER(_P)]),
+    "pkv_block_table_run": (_I32, [_P, _P, _I32, _I32, _I32, _P, _P, _I64, _I32, _I32, _I32, _P,
+                                   _I32, _I32, _c.c_float, _P, _SZ, _P, _P, _P]),
     "pkv_merge": (_I32, [_P, _P, _SZ, _P, _P, _P]),
     "pkv_gather_mla_workspace_size": (_I32, [_I32, _I32, _I32, _I32, _I32, _c.POINTER(_SZ)]),
     "pkv_gather_mla": (_I32, [_P, _P, _I64, _P, _I32, _I32, _I32, _I32, _I32, _c.c_float, _P,
@@ -262,6 +270,87 @@ def prepare_merge(plan: Plan, workspace, out, lse, stream=None):
     return call
 
 
+def _host_lengths(seq_lens_host) -> np.ndarray:
+    if hasattr(seq_lens_host, "detach"):
+        seq_lens_host = seq_lens_host.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(seq_lens_host), dtype=np.int32).reshape(-1)
+
+
+def pkv_block_table_workspace_size(seq_lens_host, num_qo_heads=32, num_kv_heads=4, head_dim=128,
+                                   page_size=16, num_cus=0, allow_split=True,
+                                   chunk_tokens=0) -> int:
+    lens = _host_lengths(seq_lens_host)
+    out = ctypes.c_size_t(0)
+    _check(lib().pkv_block_table_workspace_size(lens.ctypes.data_as(_I32P), len(lens),
+                                                num_qo_heads, num_kv_heads, head_dim, page_size,
+                                                num_cus, int(bool(allow_split)), chunk_tokens,
+                                                ctypes.byref(out)),
+           "pkv_block_table_workspace_size")
+    return int(out.value)
+
+
+def pkv_block_table_plan_create(seq_lens_host, num_qo_heads=32, num_kv_heads=4, head_dim=128,
+                                page_size=16, num_cus=0, allow_split=True, chunk_tokens=0,
+                                workspace=None, stream=None) -> Plan:
+    lens = _host_lengths(seq_lens_host)
+    if workspace is not None:
+        _require(workspace, "workspace", (__import__("torch").uint8,))
+    handle = ctypes.c_void_p(0)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    st = 0 if workspace is None else _stream(stream)
+    _check(lib().pkv_block_table_plan_create(lens.ctypes.data_as(_I32P), len(lens), num_qo_heads,
+                                             num_kv_heads, head_dim, page_size, num_cus,
+                                             int(bool(allow_split)), chunk_tokens,
+                                             _ptr(workspace), ws_bytes, st, ctypes.byref(handle)),
+           "pkv_block_table_plan_create")
+    return Plan(handle.value, len(lens), int(lens.astype(np.int64).sum()))
+
+
+def _block_table_args(plan: Plan, q, k_pool, v_pool, block_table, sm_scale, workspace, out, lse,
+                      stream):
+    import torch
+    bf = _bf16_types()
+    _require(q, "q", bf)
+    _require(k_pool, "k_pool", bf)
+    _require(v_pool, "v_pool", bf)
+    _require(block_table, "block_table", (torch.int32,))
+    _require(workspace, "workspace", (torch.uint8,))
+    _require(out, "out", bf)
+    _require(lse, "lse", (torch.float32,))
+    if q.dim() != 3 or k_pool.dim() != 4 or block_table.dim() != 2:
+        raise ValueError("q must be [B, Hq, D], the pools [pages, page_size, Hkv, D] and "
+                         "block_table [B, max_pages]")
+    if tuple(k_pool.shape) != tuple(v_pool.shape):
+        raise ValueError("k_pool and v_pool must have the same shape")
+    if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != tuple(q.shape[:2]):
+        raise ValueError("out must be shaped like q and lse like q.shape[:2]")
+    return (plan.handle, _ptr(q), q.shape[0], q.shape[1], q.shape[2], _ptr(k_pool), _ptr(v_pool),
+            k_pool.shape[0], k_pool.shape[1], k_pool.shape[2], k_pool.shape[3], _ptr(block_table),
+            block_table.shape[0], block_table.shape[1], float(sm_scale), _ptr(workspace),
+            workspace.numel(), _ptr(out), _ptr(lse), _stream(stream))
+
+
+def pkv_block_table_run(plan: Plan, q, k_pool, v_pool, block_table, sm_scale, workspace, out,
+                        lse, stream=None):
+    _check(lib().pkv_block_table_run(*_block_table_args(plan, q, k_pool, v_pool, block_table,
+                                                        sm_scale, workspace, out, lse, stream)),
+           "pkv_block_table_run")
+
+
+def prepare_block_table_run(plan: Plan, q, k_pool, v_pool, block_table, sm_scale, workspace, out,
+                            lse, stream=None):
+    """Like prepare_run, for pkv_block_table_run."""
+    args = _block_table_args(plan, q, k_pool, v_pool, block_table, sm_scale, workspace, out, lse,
+                             stream)
+    fn = plan._lib.pkv_block_table_run
+
+    def call():
+        st = fn(*args)
+        if st != PKV_OK:
+            _check(st, "pkv_block_table_run")
+    return call
+
+
 def pkv_merge(plan: Plan, workspace, out, lse, stream=None):
     _check(lib().pkv_merge(plan.handle, _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse),
                            _stream(stream)),
@@ -321,6 +410,32 @@ def decode(q, k_pool, v_pool, kv_indptr, kv_indices, sm_scale: Optional[float] =
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
     pkv_run(plan, q, k_pool, v_pool, kv_indptr, kv_indices, sm_scale, ws, out, lse, stream)
+    pkv_merge(plan, ws, out, lse, stream)
+    return out, lse
+
+
+def decode_block_table(q, k_pool, v_pool, block_table, seq_lens_host,
+                       sm_scale: Optional[float] = None, allow_split=True, chunk_tokens=0,
+                       num_cus=0, stream=None):
+    """Plan, run and merge one paged GQA decode through a block table.
+
+    ``k_pool``/``v_pool`` are ``[pages, page_size, Hkv, D]``; ``block_table``
+    is a device ``int32 [B, max_pages]``; ``seq_lens_host`` the host lengths.
+    Returns ``(out, lse)`` (bf16, fp32 base 2).
+    """
+    import torch
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(q.shape[-1])
+    ws_bytes = pkv_block_table_workspace_size(seq_lens_host, q.shape[1], k_pool.shape[2],
+                                              q.shape[2], k_pool.shape[1], num_cus, allow_split,
+                                              chunk_tokens)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    plan = pkv_block_table_plan_create(seq_lens_host, q.shape[1], k_pool.shape[2], q.shape[2],
+                                       k_pool.shape[1], num_cus, allow_split, chunk_tokens, ws,
+                                       stream)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    pkv_block_table_run(plan, q, k_pool, v_pool, block_table, sm_scale, ws, out, lse, stream)
     pkv_merge(plan, ws, out, lse, stream)
     return out, lse
 

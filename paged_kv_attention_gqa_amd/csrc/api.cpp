@@ -3,6 +3,8 @@
 // rejected call has no effect on the device.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -20,6 +22,8 @@ struct pkv_plan {
   int32_t batch;
   int32_t num_qo_heads, num_kv_heads, head_dim, page_size;
   int32_t num_cus, allow_split;
+  bool block_table;              // built from sequence lengths for pkv_block_table_run
+  int64_t max_seq_pages;         // block-table plans: most pages any sequence needs
   pkv::Partition part;
   std::vector<int32_t> tables;   // worker offsets, segments, merge records, as uploaded
   size_t off_wptr, off_segs, off_merges, off_part_o, off_part_lse, ws_bytes;
@@ -50,8 +54,12 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+constexpr int32_t kMaxPageSize = 1024;
+
+// Page sizes: exactly 1 for the CSR list, a power of two up to kMaxPageSize
+// for block tables.
 pkv_status check_gqa_shape(int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
-                           int32_t page_size) {
+                           int32_t page_size, bool block_table) {
   if (num_qo_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || page_size <= 0)
     return fail(PKV_ERR_INVALID_ARG, "head counts, head_dim and page_size must be positive");
   if (num_qo_heads % num_kv_heads != 0)
@@ -63,9 +71,20 @@ pkv_status check_gqa_shape(int32_t num_qo_heads, int32_t num_kv_heads, int32_t h
     return fail(PKV_ERR_UNSUPPORTED, "expected num_kv_heads=%d, got %d", pkv::kHkv, num_kv_heads);
   if (head_dim != pkv::kHeadDim)
     return fail(PKV_ERR_UNSUPPORTED, "expected head_dim=%d, got %d", pkv::kHeadDim, head_dim);
-  if (page_size != 1)
-    return fail(PKV_ERR_UNSUPPORTED, "expected page_size=1, got %d", page_size);
+  if (!block_table && page_size != 1)
+    return fail(PKV_ERR_UNSUPPORTED,
+                "expected page_size=1 for a CSR page list, got %d (use the block-table calls)",
+                page_size);
+  if (block_table && (page_size > kMaxPageSize || (page_size & (page_size - 1)) != 0))
+    return fail(PKV_ERR_UNSUPPORTED, "page_size must be a power of two <= %d, got %d",
+                kMaxPageSize, page_size);
   return PKV_OK;
+}
+
+int32_t log2_exact(int32_t x) {
+  int32_t s = 0;
+  while ((1 << s) < x) ++s;
+  return s;
 }
 
 pkv_status resolve_cus(int32_t* num_cus) {
@@ -82,12 +101,14 @@ pkv_status resolve_cus(int32_t* num_cus) {
 }
 
 // Builds the partition and the workspace layout of a plan (no device work).
+// kv_indptr_host holds the token offsets of the sequences (for a block-table
+// plan, the prefix sums of the sequence lengths).
 pkv_status make_plan(const int32_t* kv_indptr_host, int32_t batch, int32_t num_qo_heads,
                      int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t num_cus,
-                     int32_t allow_split, int32_t chunk_tokens, pkv_plan* p) {
+                     int32_t allow_split, int32_t chunk_tokens, bool block_table, pkv_plan* p) {
   if (kv_indptr_host == nullptr) return fail(PKV_ERR_INVALID_ARG, "kv_indptr_host is NULL");
   if (batch < 0) return fail(PKV_ERR_INVALID_ARG, "batch must be >= 0");
-  pkv_status s = check_gqa_shape(num_qo_heads, num_kv_heads, head_dim, page_size);
+  pkv_status s = check_gqa_shape(num_qo_heads, num_kv_heads, head_dim, page_size, block_table);
   if (s != PKV_OK) return s;
   if (chunk_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "chunk_tokens must be >= 0");
   s = resolve_cus(&num_cus);
@@ -103,6 +124,12 @@ pkv_status make_plan(const int32_t* kv_indptr_host, int32_t batch, int32_t num_q
   p->page_size = page_size;
   p->num_cus = num_cus;
   p->allow_split = allow_split != 0;
+  p->block_table = block_table;
+  p->max_seq_pages = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t n = static_cast<int64_t>(kv_indptr_host[b + 1]) - kv_indptr_host[b];
+    p->max_seq_pages = std::max<int64_t>(p->max_seq_pages, (n + page_size - 1) / page_size);
+  }
   p->tables.clear();
   p->tables.reserve(p->part.worker_ptr.size() + 4 * (p->part.segments.size() + p->part.merges.size()));
   p->tables.insert(p->tables.end(), p->part.worker_ptr.begin(), p->part.worker_ptr.end());
@@ -126,48 +153,37 @@ pkv_status make_plan(const int32_t* kv_indptr_host, int32_t batch, int32_t num_q
   return PKV_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* pkv_status_string(pkv_status status) {
-  switch (status) {
-    case PKV_OK: return "ok";
-    case PKV_ERR_INVALID_ARG: return "invalid argument";
-    case PKV_ERR_UNSUPPORTED: return "unsupported shape";
-    case PKV_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
-    case PKV_ERR_PLAN_MISMATCH: return "call does not match the plan";
-    case PKV_ERR_HIP: return "HIP runtime error";
+// Token offsets (prefix sums) of block-table sequence lengths.
+pkv_status offsets_from_lengths(const int32_t* seq_lens_host, int32_t batch,
+                                std::vector<int32_t>* indptr) {
+  if (seq_lens_host == nullptr && batch > 0)
+    return fail(PKV_ERR_INVALID_ARG, "seq_lens_host is NULL");
+  if (batch < 0) return fail(PKV_ERR_INVALID_ARG, "batch must be >= 0");
+  indptr->assign(static_cast<size_t>(batch) + 1, 0);
+  int64_t total = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    if (seq_lens_host[b] < 0)
+      return fail(PKV_ERR_INVALID_ARG, "seq_lens[%d] = %d is negative", b, seq_lens_host[b]);
+    total += seq_lens_host[b];
+    if (total > INT32_MAX)
+      return fail(PKV_ERR_INVALID_ARG, "the batch holds more than 2^31 - 1 tokens");
+    (*indptr)[static_cast<size_t>(b) + 1] = static_cast<int32_t>(total);
   }
-  return "unknown status";
+  return PKV_OK;
 }
 
-const char* pkv_last_error(void) { return g_last_error.c_str(); }
-
-pkv_status pkv_workspace_size(const int32_t* kv_indptr_host, int32_t batch, int32_t num_qo_heads,
-                              int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
-                              int32_t num_cus, int32_t allow_split, int32_t chunk_tokens,
-                              size_t* bytes) {
-  if (bytes == nullptr) return fail(PKV_ERR_INVALID_ARG, "bytes is NULL");
-  pkv_plan p;
-  pkv_status s = make_plan(kv_indptr_host, batch, num_qo_heads, num_kv_heads, head_dim,
-                           page_size, num_cus, allow_split, chunk_tokens, &p);
-  if (s != PKV_OK) return s;
-  *bytes = p.ws_bytes;
-  return ok();
-}
-
-pkv_status pkv_plan_create(const int32_t* kv_indptr_host, int32_t batch, int32_t num_qo_heads,
-                           int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
-                           int32_t num_cus, int32_t allow_split, int32_t chunk_tokens,
-                           void* workspace, size_t workspace_bytes, void* stream,
-                           pkv_plan** plan) {
+// Shared by pkv_plan_create and pkv_block_table_plan_create.
+pkv_status create_plan(const int32_t* kv_indptr_host, int32_t batch, int32_t num_qo_heads,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                       int32_t num_cus, int32_t allow_split, int32_t chunk_tokens,
+                       bool block_table, void* workspace, size_t workspace_bytes, void* stream,
+                       pkv_plan** plan) {
   if (plan == nullptr) return fail(PKV_ERR_INVALID_ARG, "plan is NULL");
   *plan = nullptr;
   pkv_plan* p = new (std::nothrow) pkv_plan();
   if (p == nullptr) return fail(PKV_ERR_INVALID_ARG, "out of host memory");
   pkv_status s = make_plan(kv_indptr_host, batch, num_qo_heads, num_kv_heads, head_dim,
-                           page_size, num_cus, allow_split, chunk_tokens, p);
+                           page_size, num_cus, allow_split, chunk_tokens, block_table, p);
   if (s != PKV_OK) {
     delete p;
     return s;
@@ -195,6 +211,144 @@ pkv_status pkv_plan_create(const int32_t* kv_indptr_host, int32_t batch, int32_t
   }
   *plan = p;
   return ok();
+}
+
+// Checks shared by pkv_run and pkv_block_table_run: the call against the
+// plan, pointers and alignment.
+pkv_status check_run(const pkv_plan* plan, bool block_table, const void* q, int32_t q_batch,
+                     int32_t q_heads, int32_t q_dim, const void* k_pool, const void* v_pool,
+                     int64_t num_pages, int32_t page_size, int32_t pool_kv_heads,
+                     int32_t pool_dim, float sm_scale, const void* out, const float* lse) {
+  if (plan == nullptr) return fail(PKV_ERR_INVALID_ARG, "plan is NULL");
+  if (plan->block_table != block_table)
+    return fail(PKV_ERR_PLAN_MISMATCH, block_table
+                    ? "plan was made for a CSR page list (pkv_plan_create); use pkv_run"
+                    : "plan was made for a block table (pkv_block_table_plan_create); "
+                      "use pkv_block_table_run");
+  pkv_status s = check_gqa_shape(q_heads, pool_kv_heads, q_dim, page_size, block_table);
+  if (s != PKV_OK) return s;
+  if (pool_dim != q_dim)
+    return fail(PKV_ERR_INVALID_ARG, "pool head_dim %d differs from q head_dim %d", pool_dim, q_dim);
+  if (q_batch != plan->batch || q_heads != plan->num_qo_heads || pool_kv_heads != plan->num_kv_heads ||
+      q_dim != plan->head_dim || page_size != plan->page_size)
+    return fail(PKV_ERR_PLAN_MISMATCH,
+                "call shape (B=%d, Hq=%d, Hkv=%d, D=%d, ps=%d) differs from the plan's "
+                "(B=%d, Hq=%d, Hkv=%d, D=%d, ps=%d)",
+                q_batch, q_heads, pool_kv_heads, q_dim, page_size, plan->batch,
+                plan->num_qo_heads, plan->num_kv_heads, plan->head_dim, plan->page_size);
+  if (num_pages < 0) return fail(PKV_ERR_INVALID_ARG, "num_pages must be >= 0");
+  if (plan->part.total_tokens > 0 && num_pages == 0)
+    return fail(PKV_ERR_INVALID_ARG, "the batch has tokens but the pool has no pages");
+  if (num_pages * static_cast<int64_t>(page_size) > INT32_MAX)
+    return fail(PKV_ERR_UNSUPPORTED, "the pool holds more than 2^31 - 1 token rows");
+  if (!std::isfinite(sm_scale)) return fail(PKV_ERR_INVALID_ARG, "sm_scale must be finite");
+  if (plan->batch > 0) {
+    if (q == nullptr || out == nullptr || lse == nullptr)
+      return fail(PKV_ERR_INVALID_ARG, "q, out and lse must be non-NULL");
+    if (plan->part.total_tokens > 0 && (k_pool == nullptr || v_pool == nullptr))
+      return fail(PKV_ERR_INVALID_ARG, "k_pool and v_pool must be non-NULL");
+    if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
+      return fail(PKV_ERR_INVALID_ARG, "q, k_pool, v_pool and out must be 16-byte aligned");
+  }
+  return PKV_OK;
+}
+
+// Checks the workspace against the plan, then enqueues the decode kernel.
+pkv_status launch_run(const pkv_plan* plan, const void* q, const void* k_pool, const void* v_pool,
+                      const pkv::KvAddressing& addr, float sm_scale, void* workspace,
+                      size_t workspace_bytes, void* out, float* lse, void* stream) {
+  if (plan->workspace == nullptr)
+    return fail(PKV_ERR_PLAN_MISMATCH, "host-only plan (created without a workspace)");
+  if (workspace != plan->workspace)
+    return fail(PKV_ERR_PLAN_MISMATCH, "workspace differs from the one the plan was uploaded to");
+  if (workspace_bytes < plan->ws_bytes)
+    return fail(PKV_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, plan needs %zu",
+                workspace_bytes, plan->ws_bytes);
+  if (plan->part.n_workers == 0) return ok();
+  char* ws = static_cast<char*>(workspace);
+  const float log2e = 1.4426950408889634f;
+  hipError_t e = pkv::launch_decode_partial(
+      reinterpret_cast<const int32_t*>(ws + plan->off_wptr),
+      reinterpret_cast<const int32_t*>(ws + plan->off_segs), plan->part.n_workers,
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pool),
+      static_cast<const uint16_t*>(v_pool), addr, sm_scale * log2e, static_cast<uint16_t*>(out),
+      lse, reinterpret_cast<float*>(ws + plan->off_part_o),
+      reinterpret_cast<float*>(ws + plan->off_part_lse), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_status_string(pkv_status status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_INVALID_ARG: return "invalid argument";
+    case PKV_ERR_UNSUPPORTED: return "unsupported shape";
+    case PKV_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case PKV_ERR_PLAN_MISMATCH: return "call does not match the plan";
+    case PKV_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* pkv_last_error(void) { return g_last_error.c_str(); }
+
+pkv_status pkv_workspace_size(const int32_t* kv_indptr_host, int32_t batch, int32_t num_qo_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                              int32_t num_cus, int32_t allow_split, int32_t chunk_tokens,
+                              size_t* bytes) {
+  if (bytes == nullptr) return fail(PKV_ERR_INVALID_ARG, "bytes is NULL");
+  pkv_plan p;
+  pkv_status s = make_plan(kv_indptr_host, batch, num_qo_heads, num_kv_heads, head_dim,
+                           page_size, num_cus, allow_split, chunk_tokens, false, &p);
+  if (s != PKV_OK) return s;
+  *bytes = p.ws_bytes;
+  return ok();
+}
+
+pkv_status pkv_plan_create(const int32_t* kv_indptr_host, int32_t batch, int32_t num_qo_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                           int32_t num_cus, int32_t allow_split, int32_t chunk_tokens,
+                           void* workspace, size_t workspace_bytes, void* stream,
+                           pkv_plan** plan) {
+  return create_plan(kv_indptr_host, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+                     num_cus, allow_split, chunk_tokens, false, workspace, workspace_bytes, stream,
+                     plan);
+}
+
+pkv_status pkv_block_table_workspace_size(const int32_t* seq_lens_host, int32_t batch,
+                                          int32_t num_qo_heads, int32_t num_kv_heads,
+                                          int32_t head_dim, int32_t page_size, int32_t num_cus,
+                                          int32_t allow_split, int32_t chunk_tokens,
+                                          size_t* bytes) {
+  if (bytes == nullptr) return fail(PKV_ERR_INVALID_ARG, "bytes is NULL");
+  std::vector<int32_t> indptr;
+  pkv_status s = offsets_from_lengths(seq_lens_host, batch, &indptr);
+  if (s != PKV_OK) return s;
+  pkv_plan p;
+  s = make_plan(indptr.data(), batch, num_qo_heads, num_kv_heads, head_dim, page_size, num_cus,
+                allow_split, chunk_tokens, true, &p);
+  if (s != PKV_OK) return s;
+  *bytes = p.ws_bytes;
+  return ok();
+}
+
+pkv_status pkv_block_table_plan_create(const int32_t* seq_lens_host, int32_t batch,
+                                       int32_t num_qo_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t page_size, int32_t num_cus,
+                                       int32_t allow_split, int32_t chunk_tokens, void* workspace,
+                                       size_t workspace_bytes, void* stream, pkv_plan** plan) {
+  if (plan == nullptr) return fail(PKV_ERR_INVALID_ARG, "plan is NULL");
+  *plan = nullptr;
+  std::vector<int32_t> indptr;
+  pkv_status s = offsets_from_lengths(seq_lens_host, batch, &indptr);
+  if (s != PKV_OK) return s;
+  return create_plan(indptr.data(), batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+                     num_cus, allow_split, chunk_tokens, true, workspace, workspace_bytes, stream,
+                     plan);
 }
 
 void pkv_plan_destroy(pkv_plan* plan) { delete plan; }
@@ -228,57 +382,46 @@ pkv_status pkv_run(const pkv_plan* plan, const void* q, int32_t q_batch, int32_t
                    const int32_t* kv_indptr, int64_t indptr_len, const int32_t* kv_indices,
                    int64_t num_indices, float sm_scale, void* workspace, size_t workspace_bytes,
                    void* out, float* lse, void* stream) {
-  if (plan == nullptr) return fail(PKV_ERR_INVALID_ARG, "plan is NULL");
-  pkv_status s = check_gqa_shape(q_heads, pool_kv_heads, q_dim, page_size);
+  pkv_status s = check_run(plan, false, q, q_batch, q_heads, q_dim, k_pool, v_pool, num_pages,
+                           page_size, pool_kv_heads, pool_dim, sm_scale, out, lse);
   if (s != PKV_OK) return s;
-  if (pool_dim != q_dim)
-    return fail(PKV_ERR_INVALID_ARG, "pool head_dim %d differs from q head_dim %d", pool_dim, q_dim);
-  if (q_batch != plan->batch || q_heads != plan->num_qo_heads || pool_kv_heads != plan->num_kv_heads ||
-      q_dim != plan->head_dim || page_size != plan->page_size)
-    return fail(PKV_ERR_PLAN_MISMATCH,
-                "call shape (B=%d, Hq=%d, Hkv=%d, D=%d, ps=%d) differs from the plan's "
-                "(B=%d, Hq=%d, Hkv=%d, D=%d, ps=%d)",
-                q_batch, q_heads, pool_kv_heads, q_dim, page_size, plan->batch,
-                plan->num_qo_heads, plan->num_kv_heads, plan->head_dim, plan->page_size);
   if (indptr_len != static_cast<int64_t>(plan->batch) + 1)
     return fail(PKV_ERR_INVALID_ARG, "kv_indptr has %lld entries, expected batch + 1 = %d",
                 static_cast<long long>(indptr_len), plan->batch + 1);
   if (num_indices != plan->part.total_tokens)
     return fail(PKV_ERR_INVALID_ARG, "kv_indices has %lld entries but kv_indptr[B] = %lld",
                 static_cast<long long>(num_indices), static_cast<long long>(plan->part.total_tokens));
-  if (num_pages < 0) return fail(PKV_ERR_INVALID_ARG, "num_pages must be >= 0");
-  if (num_indices > 0 && num_pages == 0)
-    return fail(PKV_ERR_INVALID_ARG, "kv_indices is non-empty but the pool has no pages");
-  if (!std::isfinite(sm_scale)) return fail(PKV_ERR_INVALID_ARG, "sm_scale must be finite");
-  if (plan->batch > 0) {
-    if (q == nullptr || out == nullptr || lse == nullptr || kv_indptr == nullptr)
-      return fail(PKV_ERR_INVALID_ARG, "q, out, lse and kv_indptr must be non-NULL");
-    if (num_indices > 0 && (k_pool == nullptr || v_pool == nullptr || kv_indices == nullptr))
-      return fail(PKV_ERR_INVALID_ARG, "k_pool, v_pool and kv_indices must be non-NULL");
-    if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
-      return fail(PKV_ERR_INVALID_ARG, "q, k_pool, v_pool and out must be 16-byte aligned");
-  }
-  if (plan->workspace == nullptr)
-    return fail(PKV_ERR_PLAN_MISMATCH, "host-only plan (created without a workspace)");
-  if (workspace != plan->workspace)
-    return fail(PKV_ERR_PLAN_MISMATCH, "workspace differs from the one the plan was uploaded to");
-  if (workspace_bytes < plan->ws_bytes)
-    return fail(PKV_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, plan needs %zu",
-                workspace_bytes, plan->ws_bytes);
-  if (plan->part.n_workers == 0) return ok();
+  if (plan->batch > 0 && kv_indptr == nullptr)
+    return fail(PKV_ERR_INVALID_ARG, "kv_indptr must be non-NULL");
+  if (num_indices > 0 && kv_indices == nullptr)
+    return fail(PKV_ERR_INVALID_ARG, "kv_indices must be non-NULL");
+  const pkv::KvAddressing addr{kv_indptr, kv_indices, 0, 0};
+  return launch_run(plan, q, k_pool, v_pool, addr, sm_scale, workspace, workspace_bytes, out, lse,
+                    stream);
+}
 
-  char* ws = static_cast<char*>(workspace);
-  const float log2e = 1.4426950408889634f;
-  hipError_t e = pkv::launch_decode_partial(
-      reinterpret_cast<const int32_t*>(ws + plan->off_wptr),
-      reinterpret_cast<const int32_t*>(ws + plan->off_segs), plan->part.n_workers,
-      static_cast<const uint16_t*>(q),
-      static_cast<const uint16_t*>(k_pool), static_cast<const uint16_t*>(v_pool), kv_indptr,
-      kv_indices, sm_scale * log2e, static_cast<uint16_t*>(out), lse,
-      reinterpret_cast<float*>(ws + plan->off_part_o), reinterpret_cast<float*>(ws + plan->off_part_lse),
-      static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
-  return ok();
+pkv_status pkv_block_table_run(const pkv_plan* plan, const void* q, int32_t q_batch,
+                               int32_t q_heads, int32_t q_dim, const void* k_pool,
+                               const void* v_pool, int64_t num_pages, int32_t page_size,
+                               int32_t pool_kv_heads, int32_t pool_dim,
+                               const int32_t* block_table, int32_t table_rows,
+                               int32_t table_cols, float sm_scale, void* workspace,
+                               size_t workspace_bytes, void* out, float* lse, void* stream) {
+  pkv_status s = check_run(plan, true, q, q_batch, q_heads, q_dim, k_pool, v_pool, num_pages,
+                           page_size, pool_kv_heads, pool_dim, sm_scale, out, lse);
+  if (s != PKV_OK) return s;
+  if (table_rows != plan->batch)
+    return fail(PKV_ERR_INVALID_ARG, "block_table has %d rows, expected batch = %d", table_rows,
+                plan->batch);
+  if (table_cols < 0 || table_cols < plan->max_seq_pages)
+    return fail(PKV_ERR_INVALID_ARG,
+                "block_table has %d columns but the longest sequence needs %lld pages",
+                table_cols, static_cast<long long>(plan->max_seq_pages));
+  if (plan->part.total_tokens > 0 && block_table == nullptr)
+    return fail(PKV_ERR_INVALID_ARG, "block_table must be non-NULL");
+  const pkv::KvAddressing addr{nullptr, block_table, table_cols, log2_exact(page_size)};
+  return launch_run(plan, q, k_pool, v_pool, addr, sm_scale, workspace, workspace_bytes, out, lse,
+                    stream);
 }
 
 pkv_status pkv_merge(const pkv_plan* plan, void* workspace, size_t workspace_bytes, void* out,

@@ -1,5 +1,5 @@
 // Paged GQA decode for gfx950 (MI355X): Hq = 32, Hkv = 4, head_dim = 128,
-// page size 1, bf16 q/K/V, fp32 accumulation, base-2 LSE.
+// bf16 q/K/V, fp32 accumulation, base-2 LSE.
 //
 // What is computed follows kernelindex.com, "flashinfer gemini-2.5-pro /
 // triton h7ykt0" (gqa_paged_decode_h32_kv4_d128_ps1, steps 4-9): gather each
@@ -7,6 +7,11 @@
 // softmax, P.V, then out = acc / l and lse = log2 of the exp-sum. The split into
 // chunks with normalised fp32 partials and an LSE merge follows the vLLM fork
 // qsa.py (_qsa_sparse_paged_gqa_splitk_kernel, _qsa_merge_splitk_kernel).
+// Pages of several tokens found through a block table follow the FlagGems
+// flash_mla_with_kvcache page (_dense_decode_kernel): token t of a sequence is
+// slot t % page_size of page table[t / page_size]. Both forms reduce to one
+// pool row index per token, (page << log2(page_size)) | slot, which is all the
+// kernel below uses; page sizes are powers of two.
 //
 // Design (gfx950, wave64):
 // * One workgroup per worker of the plan: an equal share of the batch's tokens,
@@ -157,21 +162,49 @@ __device__ __forceinline__ void compute_tile(const Tile& t, int t0, int n, const
   }
 }
 
+// Pool row (page * page_size + slot) of token j of a segment.
+template <bool kTable>
+struct TokenRows;
+
+// CSR page list, page size 1: the row is the listed page.
+template <>
+struct TokenRows<false> {
+  const int32_t* ids;   // page ids of the segment's tokens
+  __device__ TokenRows(const KvAddressing& a, int b, int lo)
+      : ids(a.ids + a.kv_indptr[b] + lo) {}
+  __device__ __forceinline__ int32_t operator()(int j) const { return ids[j]; }
+};
+
+// Block table: token t = lo + j of sequence b is slot t % ps of page row[t / ps].
+template <>
+struct TokenRows<true> {
+  const int32_t* row;   // the sequence's block-table row
+  int lo, shift, mask;
+  __device__ TokenRows(const KvAddressing& a, int b, int lo_)
+      : row(a.ids + static_cast<int64_t>(b) * a.table_stride), lo(lo_), shift(a.page_shift),
+        mask((1 << a.page_shift) - 1) {}
+  __device__ __forceinline__ int32_t operator()(int j) const {
+    const int t = lo + j;
+    return (row[t >> shift] << shift) | (t & mask);
+  }
+};
+
 // Decodes tokens [lo, lo + n) of sequence b (n > 0) with all four waves of the
 // workgroup and writes either the final out/lse (slot < 0) or a partial.
+template <bool kTable>
 __device__ __forceinline__ void process_segment(
     int b, int lo, int n, int slot, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k_pool, const uint16_t* __restrict__ v_pool,
-    const int32_t* __restrict__ kv_indptr, const int32_t* __restrict__ kv_indices,
-    float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
-    float* __restrict__ part_o, float* __restrict__ part_lse, uint16_t* lds) {
+    const KvAddressing& addr, float scale_log2, uint16_t* __restrict__ out,
+    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse,
+    uint16_t* lds) {
   const int lane = threadIdx.x & 63;
   const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // KV head of this wave
   const int r = lane & 15;
   const int c = lane >> 4;
   const int head = g * kGroup + r;   // a real query head only for r < kGroup
 
-  const int32_t* ids = kv_indices + kv_indptr[b] + lo;
+  const TokenRows<kTable> ids(addr, b, lo);
   const int last = n - 1;
 
   // Q as the B operand: lane (r, c) holds q[head r][32x + 8c, +8) for k-step x.
@@ -201,25 +234,25 @@ __device__ __forceinline__ void process_segment(
   // computed after the loop from the buffer the last pair prefetched into.
   const int n_tiles = (n + kTileTok - 1) / kTileTok;
   const int n_pairs = n_tiles / 2;
-  int32_t pa0 = ids[min(r, last)];
-  int32_t pa1 = ids[min(16 + r, last)];
-  int32_t pb0 = ids[min(32 + r, last)];
-  int32_t pb1 = ids[min(48 + r, last)];
+  int32_t pa0 = ids(min(r, last));
+  int32_t pa1 = ids(min(16 + r, last));
+  int32_t pb0 = ids(min(32 + r, last));
+  int32_t pb1 = ids(min(48 + r, last));
   Tile ta, tb;
   load_tile(ta, k_pool, v_pool, pa0, pa1, g, c);
   int t0 = 0;
   for (int pair = 0; pair < n_pairs; ++pair) {
     asm volatile("" ::: "memory");
-    pa0 = ids[min(t0 + 64 + r, last)];
-    pa1 = ids[min(t0 + 80 + r, last)];
+    pa0 = ids(min(t0 + 64 + r, last));
+    pa1 = ids(min(t0 + 80 + r, last));
     load_tile(tb, k_pool, v_pool, pb0, pb1, g, c);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
     compute_tile(ta, t0, n, qf, scale_log2, r, c, lw, st);
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
-    pb0 = ids[min(t0 + 96 + r, last)];
-    pb1 = ids[min(t0 + 112 + r, last)];
+    pb0 = ids(min(t0 + 96 + r, last));
+    pb1 = ids(min(t0 + 112 + r, last));
     load_tile(ta, k_pool, v_pool, pa0, pa1, g, c);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
@@ -256,12 +289,13 @@ __device__ __forceinline__ void process_segment(
 }
 
 // One workgroup per worker: it walks its segments in order.
+template <bool kTable>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_partial_kernel(
     const int32_t* __restrict__ worker_ptr, const int32_t* __restrict__ segments,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
-    const uint16_t* __restrict__ v_pool, const int32_t* __restrict__ kv_indptr,
-    const int32_t* __restrict__ kv_indices, float scale_log2, uint16_t* __restrict__ out,
-    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse) {
+    const uint16_t* __restrict__ v_pool, KvAddressing addr, float scale_log2,
+    uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
+    float* __restrict__ part_lse) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[kHkv * kWaveLdsU16];
   const int s_end = worker_ptr[blockIdx.x + 1];
   for (int s = worker_ptr[blockIdx.x]; s < s_end; ++s) {
@@ -269,8 +303,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int lo = seg[1];
     const int n = seg[2] - lo;
     if (n > 0)
-      process_segment(seg[0], lo, n, seg[3], q, k_pool, v_pool, kv_indptr, kv_indices,
-                      scale_log2, out, lse, part_o, part_lse, lds);
+      process_segment<kTable>(seg[0], lo, n, seg[3], q, k_pool, v_pool, addr, scale_log2, out,
+                              lse, part_o, part_lse, lds);
   }
 }
 
@@ -342,14 +376,18 @@ __global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ 
 hipError_t launch_decode_partial(const int32_t* worker_ptr, const int32_t* segments,
                                  int32_t n_workers, const uint16_t* q,
                                  const uint16_t* k_pool, const uint16_t* v_pool,
-                                 const int32_t* kv_indptr, const int32_t* kv_indices,
-                                 float sm_scale_log2, uint16_t* out, float* lse,
-                                 float* part_o, float* part_lse, hipStream_t stream) {
+                                 const KvAddressing& addr, float sm_scale_log2, uint16_t* out,
+                                 float* lse, float* part_o, float* part_lse, hipStream_t stream) {
   if (n_workers <= 0) return hipSuccess;
-  hipLaunchKernelGGL(decode_partial_kernel, dim3(n_workers), dim3(kThreads), 0, stream, worker_ptr,
-                     segments, q,
-                     k_pool, v_pool, kv_indptr, kv_indices, sm_scale_log2, out, lse, part_o,
-                     part_lse);
+  if (addr.kv_indptr == nullptr) {
+    hipLaunchKernelGGL(decode_partial_kernel<true>, dim3(n_workers), dim3(kThreads), 0, stream,
+                       worker_ptr, segments, q, k_pool, v_pool, addr, sm_scale_log2, out, lse,
+                       part_o, part_lse);
+  } else {
+    hipLaunchKernelGGL(decode_partial_kernel<false>, dim3(n_workers), dim3(kThreads), 0, stream,
+                       worker_ptr, segments, q, k_pool, v_pool, addr, sm_scale_log2, out, lse,
+                       part_o, part_lse);
+  }
   return hipGetLastError();
 }
 

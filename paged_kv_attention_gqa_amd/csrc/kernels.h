@@ -10,19 +10,30 @@
 
 namespace pkv {
 
-// Paged GQA decode, Hq = 32, Hkv = 4, D = 128, page size 1.
+// Paged GQA decode, Hq = 32, Hkv = 4, D = 128.
 constexpr int kHq = 32;
 constexpr int kHkv = 4;
 constexpr int kHeadDim = 128;
+
+// How the decode kernel finds the pool row (page * page_size + slot) of
+// token t of sequence b:
+// * CSR list (kv_indptr != NULL, page size 1): row = ids[kv_indptr[b] + t];
+// * block table (kv_indptr == NULL): row = (ids[b * table_stride + (t >> page_shift)]
+//   << page_shift) | (t & (page_size - 1)).
+struct KvAddressing {
+  const int32_t* kv_indptr;
+  const int32_t* ids;
+  int64_t table_stride;
+  int32_t page_shift;
+};
 
 // One workgroup per worker; worker w decodes the segments
 // segments[worker_ptr[w] .. worker_ptr[w+1]), each (b, tok_begin, tok_end, slot).
 hipError_t launch_decode_partial(const int32_t* worker_ptr, const int32_t* segments,
                                  int32_t n_workers, const uint16_t* q,
                                  const uint16_t* k_pool, const uint16_t* v_pool,
-                                 const int32_t* kv_indptr, const int32_t* kv_indices,
-                                 float sm_scale_log2, uint16_t* out, float* lse,
-                                 float* part_o, float* part_lse, hipStream_t stream);
+                                 const KvAddressing& addr, float sm_scale_log2, uint16_t* out,
+                                 float* lse, float* part_o, float* part_lse, hipStream_t stream);
 
 // One workgroup per (merge record (b, first_slot, n_segments, 0), query head).
 hipError_t launch_merge(const int32_t* merges, int32_t n_merges, const float* part_o,

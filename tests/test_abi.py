@@ -38,7 +38,7 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_symbols()
-    assert len(names) == 10
+    assert len(names) == 13
     for name in names:
         assert hasattr(lib, name), name
         assert name in pkv.SIGNATURES, name
@@ -217,3 +217,94 @@ def test_gather_checks(lib):
     assert g(q=0) == pkv.PKV_ERR_INVALID_ARG
     assert g(T=-1) == pkv.PKV_ERR_INVALID_ARG
     assert g(out=FAKE + 4) == pkv.PKV_ERR_INVALID_ARG
+
+
+# ------------------------------------------------------------ block tables
+
+def _bt_ws(lens, **kw):
+    lens = np.asarray(lens, dtype=np.int32)
+    out = ctypes.c_size_t(0)
+    args = dict(hq=32, hkv=4, d=128, ps=16, cus=256, split=1, chunk=0)
+    args.update(kw)
+    st = pkv.lib().pkv_block_table_workspace_size(
+        lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), len(lens), args["hq"], args["hkv"],
+        args["d"], args["ps"], args["cus"], args["split"], args["chunk"], ctypes.byref(out))
+    return st, out.value
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ps=1), pkv.PKV_OK),
+    (dict(ps=16), pkv.PKV_OK),
+    (dict(ps=1024), pkv.PKV_OK),
+    (dict(ps=3), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(ps=48), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(ps=2048), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(ps=0), pkv.PKV_ERR_INVALID_ARG),
+    (dict(hq=16), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(chunk=-1), pkv.PKV_ERR_INVALID_ARG),
+])
+def test_block_table_shape_checks(lib, kw, status):
+    assert _bt_ws([5, 40], **kw)[0] == status
+
+
+def test_block_table_length_checks(lib):
+    assert _bt_ws([5, -1])[0] == pkv.PKV_ERR_INVALID_ARG
+    assert _bt_ws([2 ** 30, 2 ** 30])[0] == pkv.PKV_ERR_INVALID_ARG     # 2^31 tokens
+    assert _bt_ws([2 ** 30, 2 ** 30 - 1])[0] == pkv.PKV_OK
+    assert _bt_ws([])[0] == pkv.PKV_OK
+    out = ctypes.c_size_t(0)
+    assert lib.pkv_block_table_workspace_size(None, 2, 32, 4, 128, 16, 256, 1, 0,
+                                              ctypes.byref(out)) == pkv.PKV_ERR_INVALID_ARG
+
+
+BT_CASES = [
+    ("edge", list(EDGE_LENGTHS)),
+    ("gqa", list(np.random.default_rng(6).integers(512, 4096, size=64, endpoint=True))),
+    ("throughput", list(lognormal_lengths(np.random.default_rng(4), 256))),
+    ("all_empty", [0, 0]),
+]
+
+
+@pytest.mark.parametrize("name,lens", BT_CASES, ids=[c[0] for c in BT_CASES])
+@pytest.mark.parametrize("ps,cus,split,chunk", [(16, 256, True, 0), (64, 256, True, 0),
+                                                (16, 256, False, 0), (128, 80, True, 96)])
+def test_block_table_plan_matches_rule(lib, name, lens, ps, cus, split, chunk):
+    plan = pkv.pkv_block_table_plan_create(lens, page_size=ps, num_cus=cus, allow_split=split,
+                                           chunk_tokens=chunk)
+    assert pkv.pkv_plan_export(plan) == plan_ref.export(_indptr(lens), cus, split, chunk)
+    size = pkv.pkv_block_table_workspace_size(lens, page_size=ps, num_cus=cus,
+                                              allow_split=split, chunk_tokens=chunk)
+    assert size == pkv.pkv_workspace_size(_indptr(lens), num_cus=cus, allow_split=split,
+                                          chunk_tokens=chunk)
+
+
+def _bt_run_raw(plan_handle, **over):
+    a = dict(q=FAKE, qb=2, qh=32, qd=128, k=FAKE, v=FAKE, pages=64, ps=16, hkv=4, pd=128,
+             table=FAKE, rows=2, cols=3, scale=0.088, ws=FAKE, ws_bytes=1 << 20, out=FAKE,
+             lse=FAKE, stream=0)
+    a.update(over)
+    return pkv.lib().pkv_block_table_run(plan_handle, a["q"], a["qb"], a["qh"], a["qd"], a["k"],
+                                         a["v"], a["pages"], a["ps"], a["hkv"], a["pd"],
+                                         a["table"], a["rows"], a["cols"], a["scale"], a["ws"],
+                                         a["ws_bytes"], a["out"], a["lse"], a["stream"])
+
+
+def test_block_table_run_checks_before_any_hip_call(lib):
+    E = pkv
+    plan = pkv.pkv_block_table_plan_create([17, 40], page_size=16, num_cus=256)   # needs 2, 3 pages
+    h = plan.handle
+    assert _bt_run_raw(None) == E.PKV_ERR_INVALID_ARG
+    assert _bt_run_raw(h, ps=32) == E.PKV_ERR_PLAN_MISMATCH
+    assert _bt_run_raw(h, ps=12) == E.PKV_ERR_UNSUPPORTED
+    assert _bt_run_raw(h, rows=3) == E.PKV_ERR_INVALID_ARG
+    assert _bt_run_raw(h, cols=2) == E.PKV_ERR_INVALID_ARG
+    assert _bt_run_raw(h, table=0) == E.PKV_ERR_INVALID_ARG
+    assert _bt_run_raw(h, pages=2 ** 27) == E.PKV_ERR_UNSUPPORTED    # 2^31 token rows
+    assert _bt_run_raw(h, pages=0) == E.PKV_ERR_INVALID_ARG
+    assert _bt_run_raw(h, scale=float("nan")) == E.PKV_ERR_INVALID_ARG
+    assert _bt_run_raw(h, v=FAKE + 8) == E.PKV_ERR_INVALID_ARG
+    assert _bt_run_raw(h) == E.PKV_ERR_PLAN_MISMATCH                 # host-only plan
+    # each kind of plan is refused by the other run call
+    assert _run_raw(h, ps=16) == E.PKV_ERR_PLAN_MISMATCH
+    csr = pkv.pkv_plan_create(_indptr([17, 40]), num_cus=256)
+    assert _bt_run_raw(csr.handle, ps=1) == E.PKV_ERR_PLAN_MISMATCH

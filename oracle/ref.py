@@ -15,7 +15,9 @@ Sources (page title, then the function or step on it):
   table, sequence lengths that end inside a page).
 * [QSA page] vLLM fork, ``vllm/models/qwen4_exp/amd/ops/qsa.py``:
   ``_qsa_sparse_paged_gqa_splitk_kernel`` (normalised partials with a base-2
-  LSE) and ``_qsa_merge_splitk_kernel`` (the LSE merge).
+  LSE), ``_qsa_merge_splitk_kernel`` (the LSE merge) and
+  ``qsa_store_cache_rows`` / ``_store_qsa_rows_kernel`` (storing new rows at
+  slot positions of a paged cache).
 
 What is computed, for one query row q_h and the rows k_j, v_j it attends to:
 
@@ -151,6 +153,27 @@ def gqa_block_table_decode(q_bits, k_bits, v_bits, block_table, seq_lens, sm_sca
             v = bf16_to_f64(v_bits[pages, slots, g, :])
             out[b, heads], lse[b, heads] = attend(q[heads], k, v, sm_scale)
     return out, lse
+
+
+def kv_append(k_pool, v_pool, k_rows, v_rows, slot_mapping):
+    """Store new K/V rows into paged pools at flat slot positions.
+
+    Pools are ``[P, page_size, Hkv, D]`` and rows ``[n, Hkv, D]`` (any dtype;
+    the rows are copied bit for bit). Row ``i`` goes to page
+    ``slot // page_size``, position ``slot % page_size`` with
+    ``slot = slot_mapping[i]``; a slot outside ``[0, P * page_size)`` (e.g.
+    -1 for padding) stores nothing ([QSA page] ``_store_qsa_rows_kernel``:
+    the validity test, page and position from the quotient and remainder).
+    Rows are applied in order. Returns new pools; the inputs are not modified.
+    """
+    k_out = np.array(k_pool, copy=True)
+    v_out = np.array(v_pool, copy=True)
+    num_pages, page_size = k_out.shape[0], k_out.shape[1]
+    for i, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64).tolist()):
+        if 0 <= slot < num_pages * page_size:
+            k_out[slot // page_size, slot % page_size] = k_rows[i]
+            v_out[slot // page_size, slot % page_size] = v_rows[i]
+    return k_out, v_out
 
 
 def merge_lse2(parts_out: np.ndarray, parts_lse: np.ndarray):

@@ -499,4 +499,63 @@ def pin_bt_single_token_and_empty(ref):
         assert np.array_equal(out[1, h], _f64(w.v_pool[page, 0, h // 8]))
 
 
+# ---------------------------------------------------------------- KV append
+
+def pin_append_round_trip(ref):
+    """Each valid row reads back at its slot; every other slot keeps its bits;
+    slots -1 and P * page_size store nothing."""
+    rng = np.random.default_rng(51)
+    pages, ps = 6, 4
+    k = rng.integers(0, 1 << 16, size=(pages, ps, 2, 8), dtype=np.uint16)
+    v = rng.integers(0, 1 << 16, size=(pages, ps, 2, 8), dtype=np.uint16)
+    slots = np.array([5, -1, 0, 23, 24, 13, -7], dtype=np.int64)
+    kr = rng.integers(0, 1 << 16, size=(7, 2, 8), dtype=np.uint16)
+    vr = rng.integers(0, 1 << 16, size=(7, 2, 8), dtype=np.uint16)
+    k2, v2 = ref.kv_append(k, v, kr, vr, slots)
+    flat_k = k2.reshape(pages * ps, 2, 8)
+    flat_v = v2.reshape(pages * ps, 2, 8)
+    written = {5: 0, 0: 2, 23: 3, 13: 5}
+    for slot in range(pages * ps):
+        if slot in written:
+            assert np.array_equal(flat_k[slot], kr[written[slot]])
+            assert np.array_equal(flat_v[slot], vr[written[slot]])
+        else:
+            assert np.array_equal(flat_k[slot], k.reshape(-1, 2, 8)[slot])
+            assert np.array_equal(flat_v[slot], v.reshape(-1, 2, 8)[slot])
+    assert np.array_equal(k, k.copy())      # inputs untouched
+    k3, _ = ref.kv_append(k, v, kr[:0], vr[:0], slots[:0])
+    assert np.array_equal(k3, k)
+
+
+def pin_append_then_decode(ref):
+    """Appending a sequence's next token at the slot after its last one gives
+    the decode of the longer sequence (the row enters the softmax)."""
+    w = make_block_table(52, [5, 16, 30], 16, extra_cols=1, pool_pages=8)
+    new_k = bf16_bits_from_f32(np.random.default_rng(53).standard_normal(
+        (3, w.num_kv_heads, w.head_dim)).astype(np.float32))
+    new_v = bf16_bits_from_f32(np.random.default_rng(54).standard_normal(
+        (3, w.num_kv_heads, w.head_dim)).astype(np.float32))
+    table = w.block_table.copy()
+    spare = [p for p in range(w.num_pages)
+             if p not in set(table[b, j] for b in range(3) for j in range(w.pages_per_seq[b]))]
+    slots = []
+    for b, n in enumerate(w.lengths):
+        if n % 16 == 0:                       # a full last page: the next token opens a new one
+            table[b, n // 16] = spare.pop()
+        slots.append(int(table[b, n // 16]) * 16 + int(n % 16))
+    k2, v2 = ref.kv_append(w.k_pool, w.v_pool, new_k, new_v, np.array(slots))
+    out, lse = ref.gqa_block_table_decode(w.q, k2, v2, table, w.seq_lens + 1, w.sm_scale)
+    for b, n in enumerate(w.lengths):
+        rows = [(int(table[b, j // 16]), j % 16) for j in range(int(n))]
+        kk = np.stack([_f64(w.k_pool[p, s]) for p, s in rows] + [_f64(new_k[b])])
+        vv = np.stack([_f64(w.v_pool[p, s]) for p, s in rows] + [_f64(new_v[b])])
+        q = _f64(w.q[b])
+        for h in range(0, 32, 5):
+            g = h // 8
+            s = w.sm_scale * (kk[:, g] @ q[h])
+            e = np.exp(s - s.max())
+            assert np.max(np.abs(out[b, h] - (e @ vv[:, g]) / e.sum())) <= 1e-12
+            assert abs(lse[b, h] - (s.max() + np.log(e.sum())) / math.log(2.0)) <= 1e-12
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

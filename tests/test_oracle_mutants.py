@@ -48,6 +48,11 @@ MUTANTS = {
                        "j = np.arange(-(-int(seq_lens[b]) // page_size) * page_size, dtype=np.int64)"),
     "bt_one_short": ("j = np.arange(int(seq_lens[b]), dtype=np.int64)",
                      "j = np.arange(max(int(seq_lens[b]) - 1, 0), dtype=np.int64)"),
+    "append_slot_swapped": ("k_out[slot // page_size, slot % page_size] = k_rows[i]",
+                            "k_out[slot % num_pages, slot // num_pages] = k_rows[i]"),
+    "append_upper_bound_dropped": ("if 0 <= slot < num_pages * page_size:", "if 0 <= slot:"),
+    "append_v_from_k": ("v_out[slot // page_size, slot % page_size] = v_rows[i]",
+                        "v_out[slot // page_size, slot % page_size] = k_rows[i]"),
     "scores_transposed_q": ("s = sm_scale * (q @ k.T)", "s = sm_scale * (q[::-1] @ k.T)"),
 }
 

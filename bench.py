@@ -199,12 +199,84 @@ def bench_mla(args):
     print(json.dumps(rec), flush=True)
 
 
+APPEND_METRIC = "KV append: HBM GB/s of rows stored into the paged pools"
+APPEND_TEXT = ("KV append of 65,536 new K/V rows (4 KV heads x 128 dims bf16, 1 KB each) at random "
+               "distinct slots of page-size-16 pools of 262,144 slots (1% of slots -1 = skipped)")
+
+
+def bench_append(args):
+    """One step is one pkv_append_kv call storing 65,536 rows."""
+    import torch
+
+    import paged_kv_attention_gqa_amd as pkv
+
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(9)
+    pages, ps, n = 16384, 16, 65536
+    slots = rng.permutation(pages * ps)[:n].astype(np.int64)
+    slots[rng.choice(n, size=n // 100, replace=False)] = -1
+    valid = int((slots >= 0).sum())
+    k_pool = torch.zeros((pages, ps, 4, 128), dtype=torch.bfloat16, device=dev)
+    v_pool = torch.zeros_like(k_pool)
+    reps = args.replicas or 3
+    rows = [(torch.randn((n, 4, 128), device=dev).to(torch.bfloat16),
+             torch.randn((n, 4, 128), device=dev).to(torch.bfloat16)) for _ in range(reps)]
+    slot_t = torch.from_numpy(slots).to(dev)
+    for i in range(args.warmup):
+        pkv.pkv_append_kv(k_pool, v_pool, *rows[i % reps], slot_t)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        pkv.pkv_append_kv(k_pool, v_pool, *rows[i % reps], slot_t)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    call_s = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
+    alg = 4096 * valid + 8 * n
+    rec = {
+        "metric": APPEND_METRIC, "value": round(alg / wall / 1e9, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3, 5), "us_per_call": round(wall * 1e6, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (random bf16 rows, random distinct slots, 1% padding)",
+        "config": {"workload": APPEND_TEXT, "name": "append", "rows": n, "valid_rows": valid,
+                   "row_replicas": reps},
+        "roofline": {"bound": "hbm", "achieved": round(alg / call_s / 1e9, 2),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(alg / call_s / 1e9 / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "append_kernel", "call_avg_us": round(call_s * 1e6, 3),
+                     "algorithmic_bytes_per_launch": alg},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import ref
+        kp = np.zeros((pages, ps, 4, 128), np.uint16)
+        kr = rows[0][0].view(torch.int16).cpu().numpy().view(np.uint16)
+        vr = rows[0][1].view(torch.int16).cpu().numpy().view(np.uint16)
+        reps_cpu, t_cpu = 0, 0.0
+        while t_cpu < args.cpu_budget and reps_cpu < 20:
+            t1 = time.perf_counter()
+            ref.kv_append(kp, kp, kr, vr, slots)
+            t_cpu += time.perf_counter() - t1
+            reps_cpu += 1
+        per = t_cpu / reps_cpu
+        rec["cpu_baseline"] = {"value": round(alg / per / 1e9, 4), "unit": "GB/s", "cores": 1,
+                               "kind": "oracle", "us_per_call": per * 1e6,
+                               "sample": f"whole append ({n} rows), {reps_cpu} runs, "
+                                         f"{t_cpu:.1f} s"}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="gqa", choices=sorted(WORKLOAD_TEXT) + ["mla"])
+    ap.add_argument("--config", default="gqa",
+                    choices=sorted(WORKLOAD_TEXT) + ["mla", "append"])
     ap.add_argument("--replicas", type=int, default=0, help="pool copies to rotate (0 = auto)")
     ap.add_argument("--no-split", action="store_true")
     ap.add_argument("--chunk", type=int, default=0)
@@ -228,6 +300,9 @@ def main():
 
     if args.config == "mla":
         bench_mla(args)
+        return
+    if args.config == "append":
+        bench_append(args)
         return
     dev = torch.device("cuda:0")
     w = make_config(args.config)

@@ -183,6 +183,26 @@ pkv_status pkv_merge(const pkv_plan* plan, void* workspace, size_t workspace_byt
                      void* out, float* lse, void* stream);
 
 /*
+ * KV append (vLLM fork qsa.py page, _store_qsa_rows_kernel and
+ * qsa_store_cache_rows): store n_rows new K and V rows into the pools at
+ * flat slot positions. Row i (k_rows / v_rows, bf16 [n_rows, num_kv_heads,
+ * head_dim], contiguous) goes to page slot / page_size, position
+ * slot % page_size of k_pool / v_pool (bf16 [num_pages, page_size,
+ * num_kv_heads, head_dim]) with slot = slot_mapping[i] (device int64
+ * [n_rows]); a slot outside [0, num_pages * page_size), e.g. -1 for padding,
+ * stores nothing. The rows are copied bit for bit. Valid slots must be
+ * distinct: two rows with the same slot race and the slot ends up holding
+ * one of them. Any head count and head_dim whose row is a multiple of 16
+ * bytes (at most 1 MiB) is accepted; n_rows <= 2^25. Pools and rows 16-byte
+ * aligned, slot_mapping 8-byte aligned. Asynchronous on `stream`; n_rows = 0
+ * enqueues nothing.
+ */
+pkv_status pkv_append_kv(void* k_pool, void* v_pool, int64_t num_pages, int32_t page_size,
+                         int32_t num_kv_heads, int32_t head_dim, const void* k_rows,
+                         const void* v_rows, const int64_t* slot_mapping, int64_t n_rows,
+                         void* stream);
+
+/*
  * Index-gather latent-attention decode (FlagGems flash_mla_with_kvcache page,
  * _sparse_decode_kernel in its bf16 mode). Row b attends to the pool rows
  * kv_pool[t] for every entry t = indices[b, i] with 0 <= t < pool_tokens;

@@ -23,7 +23,7 @@ __all__ = [
     "pkv_run", "pkv_merge", "pkv_gather_mla_workspace_size", "pkv_gather_mla",
     "prepare_run", "prepare_merge",
     "pkv_block_table_workspace_size", "pkv_block_table_plan_create", "pkv_block_table_run",
-    "prepare_block_table_run", "decode_block_table",
+    "prepare_block_table_run", "decode_block_table", "pkv_append_kv",
     "pkv_status_string", "pkv_last_error",
 ]
 
@@ -57,6 +57,7 @@ SIGNATURES = {
     "pkv_block_table_run": (_I32, [_P, _P, _I32, _I32, _I32, _P, _P, _I64, _I32, _I32, _I32, _P,
                                    _I32, _I32, _c.c_float, _P, _SZ, _P, _P, _P]),
     "pkv_merge": (_I32, [_P, _P, _SZ, _P, _P, _P]),
+    "pkv_append_kv": (_I32, [_P, _P, _I64, _I32, _I32, _I32, _P, _P, _P, _I64, _P]),
     "pkv_gather_mla_workspace_size": (_I32, [_I32, _I32, _I32, _I32, _I32, _c.POINTER(_SZ)]),
     "pkv_gather_mla": (_I32, [_P, _P, _I64, _P, _I32, _I32, _I32, _I32, _I32, _c.c_float, _P,
                               _SZ, _P, _P, _P]),
@@ -355,6 +356,27 @@ def pkv_merge(plan: Plan, workspace, out, lse, stream=None):
     _check(lib().pkv_merge(plan.handle, _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse),
                            _stream(stream)),
            "pkv_merge")
+
+
+def pkv_append_kv(k_pool, v_pool, k_rows, v_rows, slot_mapping, stream=None):
+    """Store k_rows / v_rows ``[n, Hkv, D]`` at the int64 ``slot_mapping`` positions
+    of the pools ``[pages, page_size, Hkv, D]`` (slots outside the pool are skipped)."""
+    import torch
+    bf = _bf16_types()
+    for t, name in ((k_pool, "k_pool"), (v_pool, "v_pool"), (k_rows, "k_rows"),
+                    (v_rows, "v_rows")):
+        _require(t, name, bf)
+    _require(slot_mapping, "slot_mapping", (torch.int64,))
+    if k_pool.dim() != 4 or tuple(v_pool.shape) != tuple(k_pool.shape):
+        raise ValueError("the pools must both be [pages, page_size, Hkv, D]")
+    n = slot_mapping.numel()
+    want = (n, k_pool.shape[2], k_pool.shape[3])
+    if tuple(k_rows.shape) != want or tuple(v_rows.shape) != want:
+        raise ValueError(f"k_rows and v_rows must be {list(want)}")
+    _check(lib().pkv_append_kv(_ptr(k_pool), _ptr(v_pool), k_pool.shape[0], k_pool.shape[1],
+                               k_pool.shape[2], k_pool.shape[3], _ptr(k_rows), _ptr(v_rows),
+                               _ptr(slot_mapping), n, _stream(stream)),
+           "pkv_append_kv")
 
 
 def pkv_gather_mla_workspace_size(batch, num_qo_heads, d_qk, d_v, topk) -> int:

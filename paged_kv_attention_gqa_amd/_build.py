@@ -9,7 +9,8 @@ import subprocess
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
 LIB_PATH = os.path.join(PKG_DIR, "libpkv.so")
-SOURCES = ["csrc/api.cpp", "csrc/plan.cpp", "csrc/decode.hip", "csrc/mla.hip"]
+SOURCES = ["csrc/api.cpp", "csrc/plan.cpp", "csrc/decode.hip", "csrc/mla.hip",
+           "csrc/append.hip"]
 
 # gfx950 only. Packed-fp32 VALU ops stay disabled; the kernels use MFMA and
 # scalar fp32 only.

@@ -14,6 +14,7 @@
 #include <vector>
 
 #include "pkv.h"
+#include "append.h"
 #include "kernels.h"
 #include "mla.h"
 #include "plan.h"
@@ -50,6 +51,7 @@ pkv_status ok() {
 }
 
 constexpr size_t kAlign = 256;
+constexpr int64_t kMaxAppendRows = int64_t(1) << 25;   // 64 threads per row in a 32-bit grid
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -442,6 +444,39 @@ pkv_status pkv_merge(const pkv_plan* plan, void* workspace, size_t workspace_byt
                                    reinterpret_cast<const float*>(ws + plan->off_part_lse),
                                    static_cast<uint16_t*>(out), lse, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+pkv_status pkv_append_kv(void* k_pool, void* v_pool, int64_t num_pages, int32_t page_size,
+                         int32_t num_kv_heads, int32_t head_dim, const void* k_rows,
+                         const void* v_rows, const int64_t* slot_mapping, int64_t n_rows,
+                         void* stream) {
+  if (num_pages < 0 || page_size <= 0 || num_kv_heads <= 0 || head_dim <= 0)
+    return fail(PKV_ERR_INVALID_ARG,
+                "num_pages must be >= 0 and page_size, num_kv_heads, head_dim positive");
+  const int64_t row_bytes = static_cast<int64_t>(num_kv_heads) * head_dim * 2;
+  if (row_bytes % 16 != 0 || row_bytes > (1 << 20))
+    return fail(PKV_ERR_UNSUPPORTED,
+                "a K/V row (num_kv_heads * head_dim bf16) must be a multiple of 16 bytes and at "
+                "most 1 MiB, got %lld bytes", static_cast<long long>(row_bytes));
+  if (num_pages > INT64_MAX / page_size / row_bytes)
+    return fail(PKV_ERR_INVALID_ARG, "pool size overflows");
+  if (n_rows < 0 || n_rows > kMaxAppendRows)
+    return fail(PKV_ERR_INVALID_ARG, "n_rows must be in [0, %lld], got %lld",
+                static_cast<long long>(kMaxAppendRows), static_cast<long long>(n_rows));
+  if (n_rows == 0) return ok();
+  if (k_rows == nullptr || v_rows == nullptr || slot_mapping == nullptr)
+    return fail(PKV_ERR_INVALID_ARG, "k_rows, v_rows and slot_mapping must be non-NULL");
+  if (num_pages > 0 && (k_pool == nullptr || v_pool == nullptr))
+    return fail(PKV_ERR_INVALID_ARG, "k_pool and v_pool must be non-NULL");
+  if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_rows) || !aligned16(v_rows) ||
+      (reinterpret_cast<uintptr_t>(slot_mapping) & 7u) != 0)
+    return fail(PKV_ERR_INVALID_ARG,
+                "pools and rows must be 16-byte aligned and slot_mapping 8-byte aligned");
+  hipError_t e = pkv::launch_append(k_pool, v_pool, num_pages * page_size, k_rows, v_rows,
+                                    slot_mapping, n_rows, static_cast<int32_t>(row_bytes),
+                                    static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "append launch: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -38,7 +38,7 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_symbols()
-    assert len(names) == 13
+    assert len(names) == 14
     for name in names:
         assert hasattr(lib, name), name
         assert name in pkv.SIGNATURES, name
@@ -308,3 +308,24 @@ def test_block_table_run_checks_before_any_hip_call(lib):
     assert _run_raw(h, ps=16) == E.PKV_ERR_PLAN_MISMATCH
     csr = pkv.pkv_plan_create(_indptr([17, 40]), num_cus=256)
     assert _bt_run_raw(csr.handle, ps=1) == E.PKV_ERR_PLAN_MISMATCH
+
+
+def test_append_checks(lib):
+    a = lambda **o: lib.pkv_append_kv(
+        o.get("k", FAKE), o.get("v", FAKE), o.get("pages", 10), o.get("ps", 16), o.get("hkv", 4),
+        o.get("d", 128), o.get("kr", FAKE), o.get("vr", FAKE), o.get("slots", FAKE),
+        o.get("n", 5), 0)
+    E = pkv
+    assert a(n=0) == E.PKV_OK                       # nothing to store: no launch
+    assert a(n=0, kr=0, vr=0, slots=0) == E.PKV_OK
+    assert a(n=-1) == E.PKV_ERR_INVALID_ARG
+    assert a(n=2 ** 25 + 1) == E.PKV_ERR_INVALID_ARG
+    assert a(ps=0) == E.PKV_ERR_INVALID_ARG
+    assert a(pages=-1) == E.PKV_ERR_INVALID_ARG
+    assert a(hkv=1, d=4) == E.PKV_ERR_UNSUPPORTED   # 8-byte rows
+    assert a(kr=0) == E.PKV_ERR_INVALID_ARG
+    assert a(slots=0) == E.PKV_ERR_INVALID_ARG
+    assert a(k=0) == E.PKV_ERR_INVALID_ARG
+    assert a(vr=FAKE + 8) == E.PKV_ERR_INVALID_ARG
+    assert a(slots=FAKE + 4) == E.PKV_ERR_INVALID_ARG
+    assert a(pages=2 ** 62) == E.PKV_ERR_INVALID_ARG

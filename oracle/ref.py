@@ -200,7 +200,7 @@ def merge_lse2(parts_out: np.ndarray, parts_lse: np.ndarray):
 
 
 def mla_gather_decode(q_bits, kv_bits, indices, sm_scale: float, d_v: int,
-                      batches=None):
+                      batches=None, attn_sink=None, topk_length=None):
     """Index-gather latent-attention decode.
 
     For row ``b`` the keys are the pool rows ``kv[t]`` for every list entry
@@ -208,15 +208,38 @@ def mla_gather_decode(q_bits, kv_bits, indices, sm_scale: float, d_v: int,
     masked and contribute nothing ([MLA page] ``_sparse_decode_kernel``, index
     masking). Scores use all ``Dqk`` dims; the values are the first ``d_v``
     dims of the same row. Every entry counts, repeated ids included.
+
+    ``topk_length`` (int per row, optional): only the first
+    ``min(max(topk_length[b], 0), topk)`` entries of row ``b`` are read
+    ([MLA page] ``HAVE_TOPK_LENGTH``: entries at or past the length masked).
+
+    ``attn_sink`` (float per query head, optional): a logit, in the same
+    natural-log units as ``sm_scale * q.k``, that joins the softmax
+    denominator with no value: ``out = sum_j e^(s_j) v_j / (sum_j e^(s_j) +
+    e^(sink_h))`` ([MLA page] ``HAVE_ATTN_SINK``: the output factor
+    ``exp(max) / (exp(lse) + exp(sink))``). The returned LSE is that of the
+    entries alone, as the page stores it before the sink is applied.
     Returns ``out [B, Hq, d_v]`` and base-2 ``lse [B, Hq]``.
     """
     batch, num_qo_heads, _ = q_bits.shape
     pool_tokens = kv_bits.shape[0]
+    topk = indices.shape[1]
     out = np.full((batch, num_qo_heads, d_v), np.nan)
     lse = np.full((batch, num_qo_heads), np.nan)
     for b in (range(batch) if batches is None else batches):
-        ids = np.asarray(indices[b], dtype=np.int64)
+        length = topk if topk_length is None else min(max(int(topk_length[b]), 0), topk)
+        ids = np.asarray(indices[b][:length], dtype=np.int64)
         ids = ids[(ids >= 0) & (ids < pool_tokens)]
         rows = bf16_to_f64(kv_bits[ids])                         # [n, Dqk]
-        out[b], lse[b] = attend(bf16_to_f64(q_bits[b]), rows, rows[:, :d_v], sm_scale)
+        q = bf16_to_f64(q_bits[b])
+        if attn_sink is None or len(ids) == 0:
+            out[b], lse[b] = attend(q, rows, rows[:, :d_v], sm_scale)
+            continue
+        sink = np.asarray(attn_sink, dtype=np.float64)            # [Hq]
+        s = sm_scale * (q @ rows.T)                               # [Hq, n]
+        m = s.max(axis=1)                                         # only keeps exp() in range
+        w = np.exp(s - m[:, None])
+        z_keys = w.sum(axis=1)
+        out[b] = (w @ rows[:, :d_v]) / (z_keys + np.exp(sink - m))[:, None]
+        lse[b] = (m + np.log(z_keys)) / LN2
     return out, lse

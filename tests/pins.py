@@ -499,6 +499,70 @@ def pin_bt_single_token_and_empty(ref):
         assert np.array_equal(out[1, h], _f64(w.v_pool[page, 0, h // 8]))
 
 
+def pin_mla_topk_length_is_a_prefix(ref):
+    """A per-row length reads exactly that prefix of the row's list; lengths
+    below 0 read nothing and above topk read the whole list."""
+    w = _small_mla()
+    lens = np.array([0, 37, 64], dtype=np.int32)
+    out, lse = ref.mla_gather_decode(w.q, w.kv_pool, w.indices, w.sm_scale, w.d_v,
+                                     topk_length=lens)
+    for b, n in enumerate(lens):
+        o1, l1 = ref.mla_gather_decode(w.q[b:b + 1], w.kv_pool, w.indices[b:b + 1, :n],
+                                       w.sm_scale, w.d_v)
+        assert np.array_equal(out[b], o1[0]) and np.array_equal(lse[b], l1[0])
+    assert np.all(out[0] == 0.0) and np.all(np.isneginf(lse[0]))
+    o2, l2 = ref.mla_gather_decode(w.q, w.kv_pool, w.indices, w.sm_scale, w.d_v,
+                                   topk_length=np.array([-5, 10 ** 6, 64], np.int32))
+    full = ref.mla_gather_decode(w.q, w.kv_pool, w.indices, w.sm_scale, w.d_v)
+    assert np.all(o2[0] == 0.0) and np.array_equal(o2[1:], full[0][1:])
+    assert np.array_equal(l2[1:], full[1][1:])
+
+
+def pin_mla_sink_as_zero_value_token(ref):
+    """The sink is one more logit whose value row is zero: torch softmax over
+    the scores with the sink appended, times the V rows with a zero row
+    appended. The LSE stays that of the entries alone."""
+    w = _small_mla()
+    rng = np.random.default_rng(61)
+    sink = rng.normal(0.0, 2.0, size=w.num_qo_heads)
+    out, lse = ref.mla_gather_decode(w.q, w.kv_pool, w.indices, w.sm_scale, w.d_v,
+                                     attn_sink=sink)
+    _, lse0 = ref.mla_gather_decode(w.q, w.kv_pool, w.indices, w.sm_scale, w.d_v)
+    assert np.array_equal(lse, lse0)
+    pool = torch.as_tensor(_f64(w.kv_pool))
+    for b in range(w.batch):
+        ids = torch.as_tensor(w.indices[b][w.indices[b] >= 0].astype(np.int64))
+        rows = pool[ids]
+        q = torch.as_tensor(_f64(w.q[b]))
+        logits = torch.cat([w.sm_scale * (q @ rows.T), torch.as_tensor(sink)[:, None]], dim=1)
+        vals = torch.cat([rows[:, :w.d_v], torch.zeros(1, w.d_v, dtype=torch.float64)], dim=0)
+        want = torch.softmax(logits, dim=1) @ vals
+        assert np.max(np.abs(out[b] - want.numpy())) <= 1e-12
+
+
+def pin_mla_sink_closed_forms(ref):
+    """One valid entry with score s: out = v * e^s / (e^s + e^sink). A sink of
+    -inf changes nothing; with no valid entry the sink leaves 0 and -inf."""
+    w = _small_mla()
+    ids = np.array([[42, -1, -1]], dtype=np.int32)
+    sink = np.linspace(-3.0, 3.0, w.num_qo_heads)
+    out, lse = ref.mla_gather_decode(w.q[:1], w.kv_pool, ids, w.sm_scale, w.d_v, attn_sink=sink)
+    q = _f64(w.q[0])
+    row = _f64(w.kv_pool[42])
+    for h in range(w.num_qo_heads):
+        s = w.sm_scale * math.fsum(float(a) * float(c) for a, c in zip(q[h], row))
+        frac = 1.0 / (1.0 + math.exp(sink[h] - s))
+        assert np.max(np.abs(out[0, h] - frac * row[:w.d_v])) <= 1e-12
+        assert abs(lse[0, h] - s / math.log(2.0)) <= 1e-12
+    o1, l1 = ref.mla_gather_decode(w.q, w.kv_pool, w.indices, w.sm_scale, w.d_v,
+                                   attn_sink=np.full(w.num_qo_heads, -np.inf))
+    o0, l0 = ref.mla_gather_decode(w.q, w.kv_pool, w.indices, w.sm_scale, w.d_v)
+    assert np.max(np.abs(o1 - o0)) <= 1e-15 and np.array_equal(l1, l0)
+    o2, l2 = ref.mla_gather_decode(w.q[:1], w.kv_pool, -np.ones((1, 4), np.int32), w.sm_scale,
+                                   w.d_v, attn_sink=sink)
+    assert np.all(o2 == 0.0) and np.all(np.isneginf(l2))
+
+
 # ---------------------------------------------------------------- KV append
 
 def pin_append_round_trip(ref):

@@ -211,6 +211,14 @@ pkv_status pkv_append_kv(void* k_pool, void* v_pool, int64_t num_pages, int32_t 
  *     out[b,h] = sum_t exp(s_t) kv[t, :d_v] / sum_t exp(s_t),
  *     s_t = sm_scale * dot(q[b,h,:], kv[t,:]),   lse[b,h] = log2 sum_t exp(s_t)
  * and out = 0, lse = -inf when no entry is valid.
+ * Optional (NULL = off), device pointers:
+ *   topk_length int32 [batch]: row b reads only its first
+ *     min(max(topk_length[b], 0), topk) entries (HAVE_TOPK_LENGTH on the page);
+ *   attn_sink fp32 [num_qo_heads]: a logit in the natural-log units of
+ *     sm_scale * q.k that joins the denominator with no value,
+ *     out[b,h] = sum_t exp(s_t) kv[t, :d_v] / (sum_t exp(s_t) + exp(attn_sink[h]))
+ *     (HAVE_ATTN_SINK); lse stays log2 sum_t exp(s_t), the entries alone, as
+ *     the page stores it before applying the sink.
  * Layouts: q bf16 [batch, num_qo_heads, d_qk]; kv_pool bf16 [pool_tokens, d_qk];
  * indices int32 [batch, topk]; out bf16 [batch, num_qo_heads, d_v];
  * lse fp32 [batch, num_qo_heads]. Compiled for d_qk = 576, d_v = 512 and
@@ -222,8 +230,8 @@ pkv_status pkv_gather_mla_workspace_size(int32_t batch, int32_t num_qo_heads, in
 pkv_status pkv_gather_mla(const void* q, const void* kv_pool, int64_t pool_tokens,
                           const int32_t* indices, int32_t topk, int32_t batch,
                           int32_t num_qo_heads, int32_t d_qk, int32_t d_v, float sm_scale,
-                          void* workspace, size_t workspace_bytes, void* out, float* lse,
-                          void* stream);
+                          const float* attn_sink, const int32_t* topk_length, void* workspace,
+                          size_t workspace_bytes, void* out, float* lse, void* stream);
 
 /* Static text for a status code. */
 const char* pkv_status_string(pkv_status status);

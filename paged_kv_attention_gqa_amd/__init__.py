@@ -60,7 +60,7 @@ SIGNATURES = {
     "pkv_append_kv": (_I32, [_P, _P, _I64, _I32, _I32, _I32, _P, _P, _P, _I64, _P]),
     "pkv_gather_mla_workspace_size": (_I32, [_I32, _I32, _I32, _I32, _I32, _c.POINTER(_SZ)]),
     "pkv_gather_mla": (_I32, [_P, _P, _I64, _P, _I32, _I32, _I32, _I32, _I32, _c.c_float, _P,
-                              _SZ, _P, _P, _P]),
+                              _P, _P, _SZ, _P, _P, _P]),
     "pkv_status_string": (_c.c_char_p, [_I32]),
     "pkv_last_error": (_c.c_char_p, []),
 }
@@ -387,12 +387,19 @@ def pkv_gather_mla_workspace_size(batch, num_qo_heads, d_qk, d_v, topk) -> int:
     return int(out.value)
 
 
-def pkv_gather_mla(q, kv_pool, indices, sm_scale, workspace, out, lse, d_v=512, stream=None):
+def pkv_gather_mla(q, kv_pool, indices, sm_scale, workspace, out, lse, d_v=512, stream=None,
+                   attn_sink=None, topk_length=None):
     import torch
     bf = _bf16_types()
     _require(q, "q", bf)
     _require(kv_pool, "kv_pool", bf)
     _require(indices, "indices", (torch.int32,))
+    _require(attn_sink, "attn_sink", (torch.float32,))
+    _require(topk_length, "topk_length", (torch.int32,))
+    if attn_sink is not None and tuple(attn_sink.shape) != (q.shape[1],):
+        raise ValueError("attn_sink must be [num_qo_heads]")
+    if topk_length is not None and tuple(topk_length.shape) != (q.shape[0],):
+        raise ValueError("topk_length must be [batch]")
     _require(workspace, "workspace", (torch.uint8,))
     _require(out, "out", bf)
     _require(lse, "lse", (torch.float32,))
@@ -405,8 +412,8 @@ def pkv_gather_mla(q, kv_pool, indices, sm_scale, workspace, out, lse, d_v=512, 
     ws_bytes = 0 if workspace is None else workspace.numel()
     _check(lib().pkv_gather_mla(_ptr(q), _ptr(kv_pool), kv_pool.shape[0], _ptr(indices),
                                 indices.shape[1], q.shape[0], q.shape[1], q.shape[2], d_v,
-                                float(sm_scale), _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse),
-                                _stream(stream)),
+                                float(sm_scale), _ptr(attn_sink), _ptr(topk_length),
+                                _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse), _stream(stream)),
            "pkv_gather_mla")
 
 
@@ -463,8 +470,11 @@ def decode_block_table(q, k_pool, v_pool, block_table, seq_lens_host,
 
 
 def gather_mla(q, kv_pool, indices, sm_scale: Optional[float] = None, d_v: int = 512,
-               stream=None):
-    """Index-gather latent decode; returns ``(out [B, Hq, d_v], lse [B, Hq])``."""
+               stream=None, attn_sink=None, topk_length=None):
+    """Index-gather latent decode; returns ``(out [B, Hq, d_v], lse [B, Hq])``.
+
+    ``attn_sink`` (fp32 [Hq]) and ``topk_length`` (int32 [B]) are optional
+    device tensors."""
     import torch
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(q.shape[-1])
@@ -473,5 +483,6 @@ def gather_mla(q, kv_pool, indices, sm_scale: Optional[float] = None, d_v: int =
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
     out = torch.empty((q.shape[0], q.shape[1], d_v), dtype=q.dtype, device=q.device)
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
-    pkv_gather_mla(q, kv_pool, indices, sm_scale, ws, out, lse, d_v, stream)
+    pkv_gather_mla(q, kv_pool, indices, sm_scale, ws, out, lse, d_v, stream, attn_sink,
+                   topk_length)
     return out, lse

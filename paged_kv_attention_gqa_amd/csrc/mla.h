@@ -23,10 +23,12 @@ constexpr int kMlaPlanCus = 256;
 int mla_workspace_bytes(int32_t batch, int32_t num_qo_heads, int32_t d_qk, int32_t d_v,
                         int32_t topk, size_t* bytes, std::string* err);
 
+// attn_sink: fp32 [num_qo_heads] or NULL; topk_length: int32 [batch] or NULL.
 hipError_t launch_gather_mla(const uint16_t* q, const uint16_t* kv_pool, int64_t pool_tokens,
                              const int32_t* indices, int32_t topk, int32_t batch,
-                             int32_t num_qo_heads, float sm_scale, void* workspace,
-                             uint16_t* out, float* lse, hipStream_t stream);
+                             int32_t num_qo_heads, float sm_scale, const float* attn_sink,
+                             const int32_t* topk_length, void* workspace, uint16_t* out,
+                             float* lse, hipStream_t stream);
 
 }  // namespace pkv
 

@@ -33,6 +33,12 @@
 //   (the padding measured fastest among 1168-1280 bytes).
 // * A masked entry loads row 0 (so the data is finite) and gets score -inf.
 //   A piece with no valid entry gives out 0 and lse -inf.
+// * Optional per-row list lengths (HAVE_TOPK_LENGTH on the page) shorten each
+//   piece to the entries before min(max(len, 0), topk). An optional sink logit
+//   per head (HAVE_ATTN_SINK) joins the softmax denominator with no value:
+//   the finished output is sum_j e^s_j v_j / (sum_j e^s_j + e^sink), applied
+//   where the output is finished (here for one piece, else in the merge), and
+//   the LSE stays that of the entries alone, as the page stores it.
 #include <hip/hip_runtime.h>
 
 #include "mla.h"
@@ -56,6 +62,7 @@ constexpr int kHeadBlock = 4 * kHeadsPerWave;      // 64 heads per workgroup
 constexpr int kQSteps = kMlaDqk / 32 / 2;          // 9 k-steps of 32 dims per half
 constexpr int kVBlocks = kMlaDv / 16 / 2;          // 16 blocks of 16 dims per half
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
@@ -191,8 +198,9 @@ __device__ __forceinline__ void softmax_pv(const uint16_t* buf, const uint8_t* v
 __global__ __launch_bounds__(kThreads) void mla_partial_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, int64_t pool_tokens,
     const int32_t* __restrict__ indices, int topk, int num_qo_heads, int per_piece,
-    float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
-    float* __restrict__ part_o, float* __restrict__ part_lse) {
+    float scale_log2, const float* __restrict__ attn_sink, const int32_t* __restrict__ topk_length,
+    uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
+    float* __restrict__ part_lse) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kBufU16];
   __shared__ uint8_t vflag[2][kTileTok];
   __shared__ f32x4 xscore[8][2][64];   // each wave's half scores, [wave][mb][lane]
@@ -211,7 +219,8 @@ __global__ __launch_bounds__(kThreads) void mla_partial_kernel(
   const bool head_ok = head < num_qo_heads;
   const bool group_ok = hb * kHeadBlock + hg * kHeadsPerWave < num_qo_heads;
   const int t_begin = piece * per_piece;
-  const int n = min(per_piece, topk - t_begin);   // entries of this piece (may be <= 0)
+  const int row_len = topk_length != nullptr ? min(max(topk_length[b], 0), topk) : topk;
+  const int n = min(per_piece, row_len - t_begin);   // entries of this piece (may be <= 0)
   const int32_t* idx = indices + static_cast<int64_t>(b) * topk + t_begin;
 
   u32x4 qf[kQSteps];
@@ -265,10 +274,14 @@ __global__ __launch_bounds__(kThreads) void mla_partial_kernel(
   float l_tot = st.l + __shfl_xor(st.l, 16);
   l_tot += __shfl_xor(l_tot, 32);
   const bool any = l_tot > 0.f;
-  const float inv = any ? 1.0f / l_tot : 0.f;
   const float lse2 = any ? st.m + __log2f(l_tot) : kNegInf;
   if (!head_ok) return;
   if (pieces == 1) {
+    // sum_j 2^(t_j) = l_tot * 2^m in the log2 domain; the sink adds 2^(sink * log2 e).
+    const float sink_rel = (attn_sink != nullptr && any)
+                               ? __builtin_amdgcn_exp2f(attn_sink[head] * kLog2e - st.m)
+                               : 0.f;
+    const float inv = any ? 1.0f / (l_tot + sink_rel) : 0.f;
     uint16_t* o = out + (static_cast<int64_t>(b) * num_qo_heads + head) * kMlaDv + 256 * half + 4 * c;
 #pragma unroll
     for (int db = 0; db < kVBlocks; ++db) {
@@ -279,6 +292,7 @@ __global__ __launch_bounds__(kThreads) void mla_partial_kernel(
     }
     if (c == 0 && half == 0) lse[static_cast<int64_t>(b) * num_qo_heads + head] = lse2;
   } else {
+    const float inv = any ? 1.0f / l_tot : 0.f;
     const int64_t slot = (static_cast<int64_t>(b) * num_qo_heads + head) * pieces + piece;
     float* o = part_o + slot * kMlaDv + 256 * half + 4 * c;
 #pragma unroll
@@ -291,7 +305,9 @@ __global__ __launch_bounds__(kThreads) void mla_partial_kernel(
 // folds the pieces in order.
 __global__ __launch_bounds__(128) void mla_merge_kernel(const float* __restrict__ part_o,
                                                         const float* __restrict__ part_lse,
-                                                        int pieces, uint16_t* __restrict__ out,
+                                                        int pieces, int num_qo_heads,
+                                                        const float* __restrict__ attn_sink,
+                                                        uint16_t* __restrict__ out,
                                                         float* __restrict__ lse) {
   const int64_t bh = blockIdx.x;
   const float* pl = part_lse + bh * pieces;
@@ -307,7 +323,11 @@ __global__ __launch_bounds__(128) void mla_merge_kernel(const float* __restrict_
       acc += wgt * *reinterpret_cast<const f32x4*>(part_o + (bh * pieces + i) * kMlaDv + 4 * threadIdx.x);
     }
   }
-  const float inv = den > 0.f ? 1.0f / den : 0.f;
+  // With a sink: sum_i 2^(lse_i) o_i / (sum_i 2^(lse_i) + 2^(sink log2 e)), all scaled by 2^-top.
+  const float sink_rel = (attn_sink != nullptr && den > 0.f)
+                             ? __builtin_amdgcn_exp2f(attn_sink[bh % num_qo_heads] * kLog2e - top)
+                             : 0.f;
+  const float inv = den > 0.f ? 1.0f / (den + sink_rel) : 0.f;
   const u32x2 wds = {static_cast<uint32_t>(bf16_bits(acc[0] * inv)) | (static_cast<uint32_t>(bf16_bits(acc[1] * inv)) << 16),
                      static_cast<uint32_t>(bf16_bits(acc[2] * inv)) | (static_cast<uint32_t>(bf16_bits(acc[3] * inv)) << 16)};
   *reinterpret_cast<u32x2*>(out + bh * kMlaDv + 4 * threadIdx.x) = wds;
@@ -344,8 +364,9 @@ int mla_workspace_bytes(int32_t batch, int32_t num_qo_heads, int32_t d_qk, int32
 
 hipError_t launch_gather_mla(const uint16_t* q, const uint16_t* kv_pool, int64_t pool_tokens,
                              const int32_t* indices, int32_t topk, int32_t batch,
-                             int32_t num_qo_heads, float sm_scale, void* workspace,
-                             uint16_t* out, float* lse, hipStream_t stream) {
+                             int32_t num_qo_heads, float sm_scale, const float* attn_sink,
+                             const int32_t* topk_length, void* workspace, uint16_t* out,
+                             float* lse, hipStream_t stream) {
   if (batch == 0) return hipSuccess;
   const int pieces = mla_pieces(batch, num_qo_heads, topk, kMlaPlanCus);
   const int per_piece = topk > 0 ? ((topk + pieces - 1) / pieces + kTileTok - 1) / kTileTok * kTileTok : 0;
@@ -354,12 +375,12 @@ hipError_t launch_gather_mla(const uint16_t* q, const uint16_t* kv_pool, int64_t
   float* part_lse = pieces > 1 ? part_o + static_cast<size_t>(batch) * num_qo_heads * pieces * kMlaDv : nullptr;
   const float scale_log2 = sm_scale * 1.4426950408889634f;
   hipLaunchKernelGGL(mla_partial_kernel, dim3(pieces, hblocks, batch), dim3(kThreads), 0, stream, q,
-                     kv_pool, pool_tokens, indices, topk, num_qo_heads, per_piece, scale_log2, out,
-                     lse, part_o, part_lse);
+                     kv_pool, pool_tokens, indices, topk, num_qo_heads, per_piece, scale_log2,
+                     attn_sink, topk_length, out, lse, part_o, part_lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pieces == 1) return e;
   hipLaunchKernelGGL(mla_merge_kernel, dim3(batch * num_qo_heads), dim3(kMlaDv / 4), 0, stream,
-                     part_o, part_lse, pieces, out, lse);
+                     part_o, part_lse, pieces, num_qo_heads, attn_sink, out, lse);
   return hipGetLastError();
 }
 

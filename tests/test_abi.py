@@ -210,13 +210,15 @@ def test_gather_checks(lib):
     g = lambda **o: lib.pkv_gather_mla(
         o.get("q", FAKE), o.get("kv", FAKE), o.get("T", 65536), o.get("idx", FAKE),
         o.get("topk", 2048), o.get("B", 32), o.get("H", 128), o.get("dqk", 576), o.get("dv", 512),
-        o.get("scale", 0.04), o.get("ws", FAKE), o.get("wsb", 1 << 30), o.get("out", FAKE),
-        o.get("lse", FAKE), 0)
+        o.get("scale", 0.04), o.get("sink", None), o.get("tlen", None), o.get("ws", FAKE),
+        o.get("wsb", 1 << 30), o.get("out", FAKE), o.get("lse", FAKE), 0)
     assert g(dqk=512) == pkv.PKV_ERR_UNSUPPORTED
     assert g(scale=float("nan")) == pkv.PKV_ERR_INVALID_ARG
     assert g(q=0) == pkv.PKV_ERR_INVALID_ARG
     assert g(T=-1) == pkv.PKV_ERR_INVALID_ARG
     assert g(out=FAKE + 4) == pkv.PKV_ERR_INVALID_ARG
+    assert g(sink=FAKE + 2) == pkv.PKV_ERR_INVALID_ARG
+    assert g(tlen=FAKE + 1) == pkv.PKV_ERR_INVALID_ARG
 
 
 # ------------------------------------------------------------ block tables

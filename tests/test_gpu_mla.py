@@ -73,3 +73,54 @@ def test_mla_shape_errors():
     with pytest.raises(ValueError):
         pkv.gather_mla(q[:, :, :512].contiguous(), to_dev(w.kv_pool)[:, :512].contiguous(),
                        to_dev(w.indices), w.sm_scale, d_v=512)
+
+
+def run_gpu_ex(w, attn_sink=None, topk_length=None):
+    sink_t = None if attn_sink is None else to_dev(np.asarray(attn_sink, np.float32))
+    len_t = None if topk_length is None else to_dev(np.asarray(topk_length, np.int32))
+    out, lse = pkv.gather_mla(to_dev(w.q), to_dev(w.kv_pool), to_dev(w.indices), w.sm_scale,
+                              d_v=w.d_v, attn_sink=sink_t, topk_length=len_t)
+    torch.cuda.synchronize()
+    return bf16_to_np(out), lse.cpu().numpy().astype(np.float64)
+
+
+def check_ex(w, got, what, attn_sink=None, topk_length=None):
+    want = ref.mla_gather_decode(w.q, w.kv_pool, w.indices, w.sm_scale, w.d_v,
+                                 attn_sink=None if attn_sink is None else
+                                 np.asarray(attn_sink, np.float32).astype(np.float64),
+                                 topk_length=topk_length)
+    assert_out_close(got[0], want[0], what + " out")
+    assert_lse_close(got[1], want[1], what + " lse")
+
+
+def test_mla_config_with_sink_and_lengths():
+    """Full-size list cut into pieces (merge path) with a sink per head and a
+    length per row, including 0, the whole list, and values outside [0, topk]."""
+    w = make_config("mla")
+    rng = np.random.default_rng(81)
+    sink = rng.normal(1.0, 2.0, size=w.num_qo_heads).astype(np.float32)
+    lens = rng.integers(0, w.topk + 1, size=w.batch).astype(np.int32)
+    lens[:5] = [0, w.topk, w.topk + 100, -3, 1]
+    check_ex(w, run_gpu_ex(w, sink, lens), "mla sink+len", sink, lens)
+    check_ex(w, run_gpu_ex(w, sink, None), "mla sink", sink, None)
+    check_ex(w, run_gpu_ex(w, None, lens), "mla len", None, lens)
+
+
+@pytest.mark.parametrize("topk", [33, 100, 640])
+def test_mla_sink_and_length_shapes(topk):
+    w = make_mla(90 + topk, batch=4, num_qo_heads=64, pool_tokens=2048, topk=topk,
+                 masked_per_row=topk // 9)
+    rng = np.random.default_rng(topk)
+    sink = rng.normal(0.0, 3.0, size=64).astype(np.float32)
+    sink[:4] = [50.0, -50.0, 0.0, np.inf]            # output ~0, no effect, even, all to the sink
+    lens = np.array([topk, topk // 2, 1, 0], np.int32)
+    check_ex(w, run_gpu_ex(w, sink, lens), f"topk={topk}", sink, lens)
+
+
+def test_mla_sink_minus_inf_is_bit_identical():
+    w = make_mla(95, batch=3, num_qo_heads=128, pool_tokens=4096, topk=640)
+    a = run_gpu_ex(w)
+    b = run_gpu_ex(w, attn_sink=np.full(128, -np.inf, np.float32))
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    c = run_gpu_ex(w, topk_length=np.full(3, 640, np.int32))
+    assert np.array_equal(a[0], c[0]) and np.array_equal(a[1], c[1])

@@ -9,11 +9,14 @@ from .configs import (  # noqa: F401
     CONFIG_NAMES,
     BlockTableWorkload,
     GqaWorkload,
+    MlaFp8Workload,
     MlaWorkload,
     bf16_bits_from_f32,
     make_block_table,
     make_config,
     make_gqa,
+    encode_fp8_rows,
     make_mla,
+    make_mla_fp8,
     lognormal_lengths,
 )

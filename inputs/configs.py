@@ -35,7 +35,8 @@ from typing import Optional, Sequence
 
 import numpy as np
 
-CONFIG_NAMES = ("tiny", "gqa", "edge", "throughput", "mla", "gqa_ps16", "gqa_ps64", "edge_ps16")
+CONFIG_NAMES = ("tiny", "gqa", "edge", "throughput", "mla", "gqa_ps16", "gqa_ps64", "edge_ps16",
+                "mla_fp8")
 
 # Sequence lengths of the edge-case batch: empty, single token, tile edges,
 # a long tail and one 32768-token sequence that holds about half the bytes.
@@ -298,9 +299,93 @@ def make_mla(seed: int, *, batch: int = 32, num_qo_heads: int = 128, d_qk: int =
                        sm_scale=float(sm_scale), d_v=d_v)
 
 
+FP8_TOKEN_BYTES = 656   # 512 e4m3 values, 4 fp32 scales, 64 bf16 values
+
+
+@dataclasses.dataclass
+class MlaFp8Workload:
+    """Inputs of one index-gather decode call over an FP8 latent pool."""
+
+    name: str
+    seed: int
+    q: np.ndarray            # uint16 bf16 bits [B, Hq, 576]
+    kv_pool: np.ndarray      # uint8 [T, 656]: e4m3 [0:512), fp32 scales [512:528), bf16 [528:656)
+    indices: np.ndarray      # int32 [B, topk]; -1 marks a masked entry
+    sm_scale: float
+    d_v: int = 512
+
+    @property
+    def batch(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def num_qo_heads(self) -> int:
+        return int(self.q.shape[1])
+
+    @property
+    def d_qk(self) -> int:
+        return int(self.q.shape[2])
+
+    @property
+    def pool_tokens(self) -> int:
+        return int(self.kv_pool.shape[0])
+
+    @property
+    def topk(self) -> int:
+        return int(self.indices.shape[1])
+
+
+def encode_fp8_rows(x: np.ndarray) -> np.ndarray:
+    """Pack float32 latent rows ``[T, 576]`` into 656-byte FP8 tokens.
+
+    Dims 0..511 are stored as e4m3 (OCP ``float8_e4m3fn``, via torch's
+    round-to-nearest conversion) of ``x / scale`` with one fp32 scale per 128
+    dims, ``scale = max|x| / 448`` over those dims (1 for an all-zero block);
+    dims 512..575 are stored as bf16. This builds cache contents only; the
+    decode reads them back.
+    """
+    import torch
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    t = x.shape[0]
+    nope = x[:, :512].reshape(t, 4, 128)
+    amax = np.abs(nope).max(axis=2)
+    scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    scaled = (nope / scale[:, :, None]).reshape(t, 512)
+    codes = torch.from_numpy(scaled).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    out = np.empty((t, FP8_TOKEN_BYTES), dtype=np.uint8)
+    out[:, :512] = codes
+    out[:, 512:528] = scale.view(np.uint8).reshape(t, 16)
+    out[:, 528:656] = bf16_bits_from_f32(x[:, 512:576]).view(np.uint8).reshape(t, 128)
+    return out
+
+
+def make_mla_fp8(seed: int, *, batch: int = 32, num_qo_heads: int = 128,
+                 pool_tokens: int = 65536, topk: int = 2048,
+                 masked_per_row: Optional[int] = None, sm_scale: Optional[float] = None,
+                 name: str = "custom") -> MlaFp8Workload:
+    """Build one index-gather decode input over an FP8 pool (same recipe as
+    ``make_mla``, the latent rows then packed by ``encode_fp8_rows``)."""
+    rng = np.random.default_rng(seed)
+    if masked_per_row is None:
+        masked_per_row = int(round(0.05 * topk))
+    q32 = _draw_bf16(rng, (batch, num_qo_heads, 576))
+    kv32 = _draw_bf16(rng, (pool_tokens, 576))
+    idx = np.empty((batch, topk), dtype=np.int32)
+    for b in range(batch):
+        idx[b] = rng.choice(pool_tokens, size=topk, replace=False).astype(np.int32)
+        if masked_per_row:
+            pos = rng.choice(topk, size=masked_per_row, replace=False)
+            idx[b, pos] = -1
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(576)
+    return MlaFp8Workload(name=name, seed=seed, q=bf16_bits_from_f32(q32),
+                          kv_pool=encode_fp8_rows(kv32), indices=idx, sm_scale=float(sm_scale))
+
+
 def make_config(name: str):
-    """The named workloads: five with page size 1 (seeds 1..5) and three
-    block-table workloads with page size 16 or 64 (seeds 6..8)."""
+    """The named workloads: five with page size 1 (seeds 1..5), three
+    block-table workloads with page size 16 or 64 (seeds 6..8) and the
+    index-gather workload over an FP8 pool (seed 10)."""
     if name == "tiny":
         return make_gqa(1, [17, 64], pool_pages=128, name="tiny")
     if name == "gqa":
@@ -321,6 +406,8 @@ def make_config(name: str):
         rng = np.random.default_rng(seed)
         lengths = rng.integers(512, 4096, size=64, endpoint=True)
         return make_block_table(seed, lengths, ps, name=name, rng=rng)
+    if name == "mla_fp8":
+        return make_mla_fp8(10, name="mla_fp8")
     if name == "edge_ps16":
         return make_block_table(8, EDGE_LENGTHS, 16, peaky_seq=EDGE_PEAKY_SEQ,
                                 const_v_seq=EDGE_CONST_V_SEQ, name="edge_ps16")

@@ -10,7 +10,8 @@ Sources (page title, then the function or step on it):
   the kernel ``gqa_paged_decode_h32_kv4_d128_ps1_kernel`` (its numbered steps
   2, 4, 7, 8 and 9) and its wrapper ``run``.
 * [MLA page] FlagGems docs, coverage page of ``flash_mla_with_kvcache.py``:
-  ``_sparse_decode_kernel`` (index masking, the 576/512 latent split) and
+  ``_sparse_decode_kernel`` (index masking, the 576/512 latent split, the
+  656-byte FP8 token and its dequantisation) and
   ``_dense_decode_kernel`` (pages of several tokens found through a block
   table, sequence lengths that end inside a page).
 * [QSA page] vLLM fork, ``vllm/models/qwen4_exp/amd/ops/qsa.py``:
@@ -197,6 +198,65 @@ def merge_lse2(parts_out: np.ndarray, parts_lse: np.ndarray):
     out[empty] = 0.0
     lse = np.where(empty, -np.inf, safe_top + np.log2(np.where(empty, 1.0, den)))
     return out, lse
+
+
+def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
+    """Decode OCP float8 e4m3 ("fn") codes: 1 sign bit, 4 exponent bits with
+    bias 7, 3 mantissa bits; exponent 0 is subnormal (m/8 * 2^-6); S.1111.111
+    is NaN and there is no infinity."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c >> 7, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e > 0, (1.0 + m / 8.0) * np.exp2(e - 7.0), (m / 8.0) * 2.0 ** -6)
+    mag = np.where((e == 15) & ((c & 7) == 7), np.nan, mag)
+    return sign * mag
+
+
+def _f32_to_bf16_bits(x) -> np.ndarray:
+    """float32 -> bfloat16 bit pattern, round to nearest, ties to even."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def dequant_fp8_rows(tokens: np.ndarray) -> np.ndarray:
+    """656-byte FP8 tokens ``[n, 656]`` -> bf16 bit patterns ``[n, 576]``.
+
+    [MLA page] FP8 sparse mode: bytes 0..511 are e4m3 values, bytes 512..527
+    four float32 scales (scale j for values 128j..128j+127), bytes 528..655
+    64 bfloat16 values. Value i is ``e4m3[i] * scale[i // 128]``, multiplied
+    in float32 and then rounded to bfloat16 (the page converts the product to
+    bf16 before both matrix products); the last 64 dims are the bf16 values
+    as stored.
+    """
+    tokens = np.ascontiguousarray(tokens, dtype=np.uint8)
+    n = tokens.shape[0]
+    vals = e4m3_to_f64(tokens[:, :512]).astype(np.float32)        # exact in float32
+    scales = tokens[:, 512:528].copy().view(np.float32).reshape(n, 4)
+    prod = (vals.reshape(n, 4, 128) * scales[:, :, None]).reshape(n, 512)   # float32 product
+    out = np.empty((n, 576), dtype=np.uint16)
+    out[:, :512] = _f32_to_bf16_bits(prod)
+    out[:, 512:] = tokens[:, 528:656].copy().view(np.uint16).reshape(n, 64)
+    return out
+
+
+def mla_gather_decode_fp8(q_bits, kv_tokens, indices, sm_scale: float, d_v: int = 512,
+                          batches=None, attn_sink=None, topk_length=None):
+    """Index-gather decode over an FP8 latent pool ``[T, 656]`` (uint8).
+
+    Each selected token is dequantised to 576 bf16 values (``dequant_fp8_rows``);
+    from there the decode is ``mla_gather_decode``: scores over all 576 dims,
+    values the first 512 ([MLA page]: the dequantised part serves as both K
+    and V). Only listed rows need dequantising; the result is the same as
+    dequantising the whole pool.
+    """
+    ids = np.asarray(indices, dtype=np.int64)
+    pool_tokens = kv_tokens.shape[0]
+    used = np.unique(ids[(ids >= 0) & (ids < pool_tokens)])
+    pool = np.zeros((pool_tokens, 576), dtype=np.uint16)
+    pool[used] = dequant_fp8_rows(kv_tokens[used])
+    return mla_gather_decode(q_bits, pool, indices, sm_scale, d_v, batches=batches,
+                             attn_sink=attn_sink, topk_length=topk_length)
 
 
 def mla_gather_decode(q_bits, kv_bits, indices, sm_scale: float, d_v: int,

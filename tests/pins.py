@@ -563,6 +563,88 @@ def pin_mla_sink_closed_forms(ref):
     assert np.all(o2 == 0.0) and np.all(np.isneginf(l2))
 
 
+# --------------------------------------------------------------- FP8 gather
+
+def pin_e4m3_decode(ref):
+    """All 256 codes against torch's float8_e4m3fn, plus hand-checked values."""
+    codes = np.arange(256, dtype=np.uint8)
+    got = ref.e4m3_to_f64(codes)
+    want = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.array_equal(got[ok], want[ok]) and np.array_equal(np.signbit(got[ok]), np.signbit(want[ok]))
+    hand = {0x38: 1.0, 0xB8: -1.0, 0x7E: 448.0, 0x01: 2.0 ** -9, 0x08: 2.0 ** -6, 0x3C: 1.5,
+            0x00: 0.0, 0x41: 2.25}
+    for c, v in hand.items():
+        assert ref.e4m3_to_f64(np.array([c], np.uint8))[0] == v, hex(c)
+    assert np.isnan(ref.e4m3_to_f64(np.array([0x7F, 0xFF], np.uint8))).all()
+
+
+def _fp8_token(codes, scales, rope_bits):
+    t = np.zeros(656, dtype=np.uint8)
+    t[:512] = codes
+    t[512:528] = np.asarray(scales, dtype=np.float32).view(np.uint8)
+    t[528:656] = np.asarray(rope_bits, dtype=np.uint16).view(np.uint8)
+    return t
+
+
+def pin_fp8_dequant_layout(ref):
+    """Value i uses scale i // 128; the last 64 dims are the stored bf16 bits."""
+    rope = np.arange(64, dtype=np.uint16) + 0x3F00
+    tok = _fp8_token(np.full(512, 0x38, np.uint8), [1.0, 2.0, 0.25, 8.0], rope)   # all codes 1.0
+    got = ref.dequant_fp8_rows(tok[None])[0]
+    want = np.concatenate([np.full(128, 0x3F80), np.full(128, 0x4000), np.full(128, 0x3E80),
+                           np.full(128, 0x4100)]).astype(np.uint16)
+    assert np.array_equal(got[:512], want)
+    assert np.array_equal(got[512:], rope)
+
+
+def pin_fp8_dequant_rounding(ref):
+    """Random codes and scales against torch: float8 -> float32, times the
+    float32 scale, rounded to bfloat16."""
+    rng = np.random.default_rng(71)
+    n = 64
+    codes = rng.integers(0, 256, size=(n, 512), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x3A                 # no NaN codes
+    scales = (rng.random((n, 4)) * 0.02 + 1e-3).astype(np.float32)
+    rope = rng.integers(0, 0x7F00, size=(n, 64), dtype=np.uint16)
+    toks = np.stack([_fp8_token(codes[i], scales[i], rope[i]) for i in range(n)])
+    got = ref.dequant_fp8_rows(toks)
+    vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float32).reshape(n, 4, 128)
+    prod = (vals * torch.from_numpy(scales)[:, :, None]).reshape(n, 512)
+    want = prod.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got[:, :512], want)
+    assert np.array_equal(got[:, 512:], rope)
+
+
+def pin_fp8_gather_matches_known_values(ref):
+    """Tokens built from values known exactly (e4m3 codes times powers of two)
+    decode to the bf16 pool of those values: the FP8 gather then equals the
+    bf16 gather over that pool."""
+    rng = np.random.default_rng(72)
+    t = 120
+    codes = rng.integers(0, 0x7E, size=(t, 512), dtype=np.uint8) | (rng.integers(0, 2, size=(t, 512), dtype=np.uint8) << 7)
+    exps = rng.integers(-8, 2, size=(t, 4))
+    scales = np.exp2(exps).astype(np.float32)
+    rope_vals = rng.standard_normal((t, 64)).astype(np.float32)
+    rope = bf16_bits_from_f32(rope_vals)
+    toks = np.stack([_fp8_token(codes[i], scales[i], rope[i]) for i in range(t)])
+    vals = np.empty((t, 576), dtype=np.float32)
+    for i in range(t):
+        for j in range(512):
+            c = int(codes[i, j])
+            e, m = (c >> 3) & 15, c & 7
+            mag = (1 + m / 8) * 2.0 ** (e - 7) if e else (m / 8) * 2.0 ** -6
+            vals[i, j] = (-mag if c >> 7 else mag) * scales[i, j // 128]
+    vals[:, 512:] = rope_vals
+    pool_bits = bf16_bits_from_f32(vals)
+    assert np.array_equal(ref.dequant_fp8_rows(toks), pool_bits)
+    w = make_mla(73, batch=2, num_qo_heads=16, pool_tokens=t, topk=40, masked_per_row=3)
+    o1, l1 = ref.mla_gather_decode_fp8(w.q, toks, w.indices, w.sm_scale)
+    o2, l2 = ref.mla_gather_decode(w.q, pool_bits, w.indices, w.sm_scale, 512)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
 # ---------------------------------------------------------------- KV append
 
 def pin_append_round_trip(ref):

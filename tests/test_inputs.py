@@ -91,3 +91,22 @@ def test_block_table_padding_and_extra_columns():
     assert list(w.pages_per_seq) == [0, 1, 1, 2]
     assert w.block_table.shape == (4, 4) and w.num_pages == 10
     assert np.all(w.block_table[0] == -1) and np.all(w.block_table[3, 2:] == -1)
+
+
+def test_fp8_pool_encoding():
+    """The packed FP8 tokens decode close to the drawn values (e4m3 keeps 3
+    mantissa bits: error <= 2^-4 of the block's max per value, plus bf16)."""
+    from inputs import encode_fp8_rows
+    from oracle import ref
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((50, 576)).astype(np.float32)
+    x[3, :128] = 0.0                                  # an all-zero block keeps scale 1
+    tok = encode_fp8_rows(x)
+    assert tok.shape == (50, 656) and tok.dtype == np.uint8
+    scales = tok[:, 512:528].copy().view(np.float32).reshape(50, 4)
+    assert scales[3, 0] == 1.0
+    dq = ref.bf16_to_f64(ref.dequant_fp8_rows(tok))
+    amax = np.abs(x[:, :512]).reshape(50, 4, 128).max(axis=2)
+    err = np.abs(dq[:, :512] - x[:, :512]).reshape(50, 4, 128)
+    assert np.all(err <= amax[:, :, None] * 2.0 ** -4 + 1e-30)
+    assert np.array_equal(ref.dequant_fp8_rows(tok)[:, 512:], bf16_bits_from_f32(x[:, 512:]))

@@ -62,6 +62,12 @@ MUTANTS = {
                     "lse[b] = (m + np.log(z_keys + np.exp(sink - m))) / LN2"),
     "sink_base_2": ("(z_keys + np.exp(sink - m))[:, None]", "(z_keys + np.exp2(sink - m))[:, None]"),
     "sink_ignored": ("(z_keys + np.exp(sink - m))[:, None]", "(z_keys)[:, None]"),
+    "e4m3_bias_8": ("(1.0 + m / 8.0) * np.exp2(e - 7.0)", "(1.0 + m / 8.0) * np.exp2(e - 8.0)"),
+    "e4m3_subnormal_scale": ("(m / 8.0) * 2.0 ** -6", "(m / 8.0) * 2.0 ** -7"),
+    "fp8_scale_index_modulo": ("(vals.reshape(n, 4, 128) * scales[:, :, None])",
+                               "(vals.reshape(n, 128, 4) * scales[:, None, :])"),
+    "fp8_rope_offset": ("tokens[:, 528:656].copy()", "tokens[:, 512:640].copy()"),
+    "fp8_no_bf16_rounding": ("((u + 0x7FFF + ((u >> 16) & 1)) >> 16)", "(u >> 16)"),
     "scores_transposed_q": ("s = sm_scale * (q @ k.T)", "s = sm_scale * (q[::-1] @ k.T)"),
 }
 

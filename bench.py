@@ -128,26 +128,34 @@ MLA_TEXT = ("index-gather MLA decode, B=32, 128 q heads, latent dim 576 (first 5
             "tokens, 2048 distinct ids per row with 102 masked (-1), sm_scale=1/sqrt(576)")
 
 
+MLA_FP8_TEXT = ("index-gather MLA decode over an FP8 pool, B=32, 128 q heads, 656-byte tokens "
+                "(512 e4m3 + 4 fp32 scales + 64 bf16; dequantised 576 dims, first 512 = V), pool "
+                "65536 tokens, 2048 distinct ids per row with 102 masked (-1), sm_scale=1/sqrt(576)")
+
+
 def bench_mla(args):
-    """Index-gather decode: one step is one pkv_gather_mla call (partials + merge)."""
+    """Index-gather decode: one step is one pkv_gather_mla (or _fp8) call (partials + merge)."""
     import torch
 
     import paged_kv_attention_gqa_amd as pkv
     from inputs import make_config
 
     dev = torch.device("cuda:0")
-    w = make_config("mla")
+    fp8 = args.config == "mla_fp8"
+    w = make_config(args.config)
     as_t = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
     q = as_t(w.q)
     reps = args.replicas or 4
-    pools = [as_t(w.kv_pool)] + [as_t(w.kv_pool).clone() for _ in range(reps - 1)]
+    as_pool = (lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)) if fp8 else as_t
+    pools = [as_pool(w.kv_pool)] + [as_pool(w.kv_pool).clone() for _ in range(reps - 1)]
+    gather = pkv.pkv_gather_mla_fp8 if fp8 else pkv.pkv_gather_mla
     idx = torch.from_numpy(w.indices).to(dev)
     ws_bytes = pkv.pkv_gather_mla_workspace_size(w.batch, w.num_qo_heads, w.d_qk, w.d_v, w.topk)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     out = torch.empty((w.batch, w.num_qo_heads, w.d_v), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((w.batch, w.num_qo_heads), dtype=torch.float32, device=dev)
     for i in range(args.warmup):
-        pkv.pkv_gather_mla(q, pools[i % reps], idx, w.sm_scale, ws, out, lse, w.d_v)
+        gather(q, pools[i % reps], idx, w.sm_scale, ws, out, lse, w.d_v)
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
@@ -155,14 +163,14 @@ def bench_mla(args):
     t0 = time.perf_counter()
     for i in range(args.steps):
         ev[i][0].record(stream)
-        pkv.pkv_gather_mla(q, pools[i % reps], idx, w.sm_scale, ws, out, lse, w.d_v)
+        gather(q, pools[i % reps], idx, w.sm_scale, ws, out, lse, w.d_v)
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / args.steps
     call_s = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
     valid = int((w.indices >= 0).sum())
     flops = 2.0 * w.num_qo_heads * valid * (w.d_qk + w.d_v)
-    gathered = 1152.0 * valid
+    gathered = (656.0 if fp8 else 1152.0) * valid
     rec = {
         "metric": MLA_METRIC, "value": round(flops / wall / 1e12, 2), "unit": "TFLOP/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -170,7 +178,9 @@ def bench_mla(args):
         "gathered_GBps": round(gathered / wall / 1e9, 1), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16 q/latent pool, uniform distinct ids, 5% masked)",
-        "config": {"workload": MLA_TEXT, "name": "mla", "valid_entries": valid,
+        "config": {"workload": MLA_FP8_TEXT if fp8 else MLA_TEXT, "name": args.config,
+                   "kv_format": "656-byte e4m3 tokens" if fp8 else "bf16 rows",
+                   "valid_entries": valid,
                    "pool_replicas": reps},
         "roofline": {"bound": "mfma", "achieved": round(flops / call_s / 1e12, 2), "peak": 2500.0,
                      "unit": "TFLOP/s", "frac": round(flops / call_s / 1e12 / 2500.0, 4),
@@ -189,7 +199,10 @@ def bench_mla(args):
         reps_cpu, t_cpu = 0, 0.0
         while t_cpu < args.cpu_budget and reps_cpu < 50:
             t1 = time.perf_counter()
-            ref.mla_gather_decode(w.q, w.kv_pool, w.indices, w.sm_scale, w.d_v)
+            if fp8:
+                ref.mla_gather_decode_fp8(w.q, w.kv_pool, w.indices, w.sm_scale, w.d_v)
+            else:
+                ref.mla_gather_decode(w.q, w.kv_pool, w.indices, w.sm_scale, w.d_v)
             t_cpu += time.perf_counter() - t1
             reps_cpu += 1
         per = t_cpu / reps_cpu
@@ -276,7 +289,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="gqa",
-                    choices=sorted(WORKLOAD_TEXT) + ["mla", "append"])
+                    choices=sorted(WORKLOAD_TEXT) + ["mla", "mla_fp8", "append"])
     ap.add_argument("--replicas", type=int, default=0, help="pool copies to rotate (0 = auto)")
     ap.add_argument("--no-split", action="store_true")
     ap.add_argument("--chunk", type=int, default=0)
@@ -298,7 +311,7 @@ def main():
     import paged_kv_attention_gqa_amd as pkv
     from inputs import make_config
 
-    if args.config == "mla":
+    if args.config in ("mla", "mla_fp8"):
         bench_mla(args)
         return
     if args.config == "append":

@@ -233,6 +233,24 @@ pkv_status pkv_gather_mla(const void* q, const void* kv_pool, int64_t pool_token
                           const float* attn_sink, const int32_t* topk_length, void* workspace,
                           size_t workspace_bytes, void* out, float* lse, void* stream);
 
+/*
+ * The same gather over a pool of FP8 latent tokens (FlagGems
+ * flash_mla_with_kvcache page, FP8 sparse mode): kv_pool is
+ * [pool_tokens, 656] bytes per token: 512 OCP e4m3 ("e4m3fn") values, then 4
+ * fp32 scales (scale k for values 128k .. 128k+127), then 64 bf16 values.
+ * Each selected token is dequantised to 576 bf16 values, value i =
+ * bf16_rne(fp32(e4m3[i]) * scale[i / 128]) for i < 512 and the stored bf16
+ * values after; the attention is then the bf16 gather above (scores over all
+ * 576 dims, values the first 512). Same arguments, options, workspace
+ * (pkv_gather_mla_workspace_size) and errors; kv_pool 16-byte aligned.
+ */
+pkv_status pkv_gather_mla_fp8(const void* q, const void* kv_pool, int64_t pool_tokens,
+                              const int32_t* indices, int32_t topk, int32_t batch,
+                              int32_t num_qo_heads, int32_t d_qk, int32_t d_v, float sm_scale,
+                              const float* attn_sink, const int32_t* topk_length,
+                              void* workspace, size_t workspace_bytes, void* out, float* lse,
+                              void* stream);
+
 /* Static text for a status code. */
 const char* pkv_status_string(pkv_status status);
 

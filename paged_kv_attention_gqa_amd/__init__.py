@@ -24,6 +24,7 @@ __all__ = [
     "prepare_run", "prepare_merge",
     "pkv_block_table_workspace_size", "pkv_block_table_plan_create", "pkv_block_table_run",
     "prepare_block_table_run", "decode_block_table", "pkv_append_kv",
+    "pkv_gather_mla_fp8", "gather_mla_fp8",
     "pkv_status_string", "pkv_last_error",
 ]
 
@@ -61,6 +62,8 @@ SIGNATURES = {
     "pkv_gather_mla_workspace_size": (_I32, [_I32, _I32, _I32, _I32, _I32, _c.POINTER(_SZ)]),
     "pkv_gather_mla": (_I32, [_P, _P, _I64, _P, _I32, _I32, _I32, _I32, _I32, _c.c_float, _P,
                               _P, _P, _SZ, _P, _P, _P]),
+    "pkv_gather_mla_fp8": (_I32, [_P, _P, _I64, _P, _I32, _I32, _I32, _I32, _I32, _c.c_float,
+                                  _P, _P, _P, _SZ, _P, _P, _P]),
     "pkv_status_string": (_c.c_char_p, [_I32]),
     "pkv_last_error": (_c.c_char_p, []),
 }
@@ -389,10 +392,23 @@ def pkv_gather_mla_workspace_size(batch, num_qo_heads, d_qk, d_v, topk) -> int:
 
 def pkv_gather_mla(q, kv_pool, indices, sm_scale, workspace, out, lse, d_v=512, stream=None,
                    attn_sink=None, topk_length=None):
+    _gather(False, q, kv_pool, indices, sm_scale, workspace, out, lse, d_v, stream, attn_sink,
+            topk_length)
+
+
+def pkv_gather_mla_fp8(q, kv_pool, indices, sm_scale, workspace, out, lse, d_v=512, stream=None,
+                       attn_sink=None, topk_length=None):
+    """Like pkv_gather_mla over a uint8 pool of 656-byte FP8 tokens ``[T, 656]``."""
+    _gather(True, q, kv_pool, indices, sm_scale, workspace, out, lse, d_v, stream, attn_sink,
+            topk_length)
+
+
+def _gather(fp8, q, kv_pool, indices, sm_scale, workspace, out, lse, d_v, stream, attn_sink,
+            topk_length):
     import torch
     bf = _bf16_types()
     _require(q, "q", bf)
-    _require(kv_pool, "kv_pool", bf)
+    _require(kv_pool, "kv_pool", (torch.uint8,) if fp8 else bf)
     _require(indices, "indices", (torch.int32,))
     _require(attn_sink, "attn_sink", (torch.float32,))
     _require(topk_length, "topk_length", (torch.int32,))
@@ -404,17 +420,19 @@ def pkv_gather_mla(q, kv_pool, indices, sm_scale, workspace, out, lse, d_v=512, 
     _require(out, "out", bf)
     _require(lse, "lse", (torch.float32,))
     if q.dim() != 3 or kv_pool.dim() != 2 or indices.dim() != 2:
-        raise ValueError("q must be [B, Hq, Dqk], kv_pool [T, Dqk], indices [B, topk]")
-    if kv_pool.shape[1] != q.shape[2] or indices.shape[0] != q.shape[0]:
-        raise ValueError("kv_pool width must equal q's and indices must have one row per query")
+        raise ValueError("q must be [B, Hq, Dqk], kv_pool [T, width], indices [B, topk]")
+    width = 656 if fp8 else q.shape[2]
+    if kv_pool.shape[1] != width or indices.shape[0] != q.shape[0]:
+        raise ValueError(f"kv_pool rows must have {width} elements and indices one row per query")
     if tuple(out.shape) != (q.shape[0], q.shape[1], d_v) or tuple(lse.shape) != tuple(q.shape[:2]):
         raise ValueError("out must be [B, Hq, d_v] and lse [B, Hq]")
     ws_bytes = 0 if workspace is None else workspace.numel()
-    _check(lib().pkv_gather_mla(_ptr(q), _ptr(kv_pool), kv_pool.shape[0], _ptr(indices),
+    fn = lib().pkv_gather_mla_fp8 if fp8 else lib().pkv_gather_mla
+    _check(fn(_ptr(q), _ptr(kv_pool), kv_pool.shape[0], _ptr(indices),
                                 indices.shape[1], q.shape[0], q.shape[1], q.shape[2], d_v,
                                 float(sm_scale), _ptr(attn_sink), _ptr(topk_length),
                                 _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse), _stream(stream)),
-           "pkv_gather_mla")
+           "pkv_gather_mla_fp8" if fp8 else "pkv_gather_mla")
 
 
 # ------------------------------------------------------------ conveniences
@@ -469,8 +487,15 @@ def decode_block_table(q, k_pool, v_pool, block_table, seq_lens_host,
     return out, lse
 
 
+def gather_mla_fp8(q, kv_pool, indices, sm_scale: Optional[float] = None, d_v: int = 512,
+                   stream=None, attn_sink=None, topk_length=None):
+    """Index-gather latent decode over a uint8 FP8 pool ``[T, 656]``."""
+    return gather_mla(q, kv_pool, indices, sm_scale, d_v, stream, attn_sink, topk_length,
+                      _fp8=True)
+
+
 def gather_mla(q, kv_pool, indices, sm_scale: Optional[float] = None, d_v: int = 512,
-               stream=None, attn_sink=None, topk_length=None):
+               stream=None, attn_sink=None, topk_length=None, _fp8=False):
     """Index-gather latent decode; returns ``(out [B, Hq, d_v], lse [B, Hq])``.
 
     ``attn_sink`` (fp32 [Hq]) and ``topk_length`` (int32 [B]) are optional
@@ -483,6 +508,6 @@ def gather_mla(q, kv_pool, indices, sm_scale: Optional[float] = None, d_v: int =
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
     out = torch.empty((q.shape[0], q.shape[1], d_v), dtype=q.dtype, device=q.device)
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
-    pkv_gather_mla(q, kv_pool, indices, sm_scale, ws, out, lse, d_v, stream, attn_sink,
-                   topk_length)
+    _gather(_fp8, q, kv_pool, indices, sm_scale, ws, out, lse, d_v, stream, attn_sink,
+            topk_length)
     return out, lse

@@ -282,6 +282,42 @@ pkv_status launch_run(const pkv_plan* plan, const void* q, const void* k_pool, c
 
 }  // namespace
 
+namespace {
+
+pkv_status gather_common(const void* q, const void* kv_pool, bool fp8_pool, int64_t pool_tokens,
+                         const int32_t* indices, int32_t topk, int32_t batch, int32_t num_qo_heads,
+                         int32_t d_qk, int32_t d_v, float sm_scale, const float* attn_sink,
+                         const int32_t* topk_length, void* workspace, size_t workspace_bytes,
+                         void* out, float* lse, void* stream) {
+  std::string err;
+  size_t need = 0;
+  int code = pkv::mla_workspace_bytes(batch, num_qo_heads, d_qk, d_v, topk, &need, &err);
+  if (code != 0) return fail(static_cast<pkv_status>(code), "%s", err.c_str());
+  if (pool_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "pool_tokens must be >= 0");
+  if (!std::isfinite(sm_scale)) return fail(PKV_ERR_INVALID_ARG, "sm_scale must be finite");
+  if (batch == 0) return ok();
+  if (q == nullptr || indices == nullptr || out == nullptr || lse == nullptr)
+    return fail(PKV_ERR_INVALID_ARG, "q, indices, out and lse must be non-NULL");
+  if (pool_tokens > 0 && kv_pool == nullptr) return fail(PKV_ERR_INVALID_ARG, "kv_pool is NULL");
+  if (!aligned16(q) || !aligned16(kv_pool) || !aligned16(out) || !aligned16(workspace))
+    return fail(PKV_ERR_INVALID_ARG, "q, kv_pool, out and workspace must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(attn_sink) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(topk_length) & 3u) != 0)
+    return fail(PKV_ERR_INVALID_ARG, "attn_sink and topk_length must be 4-byte aligned");
+  if (need > 0 && workspace == nullptr) return fail(PKV_ERR_INVALID_ARG, "workspace is NULL");
+  if (workspace_bytes < need)
+    return fail(PKV_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, gather needs %zu",
+                workspace_bytes, need);
+  hipError_t e = pkv::launch_gather_mla(
+      static_cast<const uint16_t*>(q), kv_pool, fp8_pool, pool_tokens, indices, topk, batch,
+      num_qo_heads, sm_scale, attn_sink, topk_length, workspace, static_cast<uint16_t*>(out), lse,
+      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "gather launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* pkv_status_string(pkv_status status) {
@@ -496,31 +532,20 @@ pkv_status pkv_gather_mla(const void* q, const void* kv_pool, int64_t pool_token
                           int32_t num_qo_heads, int32_t d_qk, int32_t d_v, float sm_scale,
                           const float* attn_sink, const int32_t* topk_length, void* workspace,
                           size_t workspace_bytes, void* out, float* lse, void* stream) {
-  std::string err;
-  size_t need = 0;
-  int code = pkv::mla_workspace_bytes(batch, num_qo_heads, d_qk, d_v, topk, &need, &err);
-  if (code != 0) return fail(static_cast<pkv_status>(code), "%s", err.c_str());
-  if (pool_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "pool_tokens must be >= 0");
-  if (!std::isfinite(sm_scale)) return fail(PKV_ERR_INVALID_ARG, "sm_scale must be finite");
-  if (batch == 0) return ok();
-  if (q == nullptr || indices == nullptr || out == nullptr || lse == nullptr)
-    return fail(PKV_ERR_INVALID_ARG, "q, indices, out and lse must be non-NULL");
-  if (pool_tokens > 0 && kv_pool == nullptr) return fail(PKV_ERR_INVALID_ARG, "kv_pool is NULL");
-  if (!aligned16(q) || !aligned16(kv_pool) || !aligned16(out) || !aligned16(workspace))
-    return fail(PKV_ERR_INVALID_ARG, "q, kv_pool, out and workspace must be 16-byte aligned");
-  if ((reinterpret_cast<uintptr_t>(attn_sink) & 3u) != 0 ||
-      (reinterpret_cast<uintptr_t>(topk_length) & 3u) != 0)
-    return fail(PKV_ERR_INVALID_ARG, "attn_sink and topk_length must be 4-byte aligned");
-  if (need > 0 && workspace == nullptr) return fail(PKV_ERR_INVALID_ARG, "workspace is NULL");
-  if (workspace_bytes < need)
-    return fail(PKV_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, gather needs %zu",
-                workspace_bytes, need);
-  hipError_t e = pkv::launch_gather_mla(
-      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv_pool), pool_tokens, indices,
-      topk, batch, num_qo_heads, sm_scale, attn_sink, topk_length, workspace,
-      static_cast<uint16_t*>(out), lse, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(PKV_ERR_HIP, "gather launch: %s", hipGetErrorString(e));
-  return ok();
+  return gather_common(q, kv_pool, false, pool_tokens, indices, topk, batch, num_qo_heads, d_qk,
+                       d_v, sm_scale, attn_sink, topk_length, workspace, workspace_bytes, out,
+                       lse, stream);
+}
+
+pkv_status pkv_gather_mla_fp8(const void* q, const void* kv_pool, int64_t pool_tokens,
+                              const int32_t* indices, int32_t topk, int32_t batch,
+                              int32_t num_qo_heads, int32_t d_qk, int32_t d_v, float sm_scale,
+                              const float* attn_sink, const int32_t* topk_length,
+                              void* workspace, size_t workspace_bytes, void* out, float* lse,
+                              void* stream) {
+  return gather_common(q, kv_pool, true, pool_tokens, indices, topk, batch, num_qo_heads, d_qk,
+                       d_v, sm_scale, attn_sink, topk_length, workspace, workspace_bytes, out,
+                       lse, stream);
 }
 
 }  // extern "C"

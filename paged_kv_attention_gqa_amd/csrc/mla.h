@@ -14,6 +14,8 @@ namespace pkv {
 constexpr int kMlaDqk = 576;
 constexpr int kMlaDv = 512;
 constexpr int kMlaMaxHeads = 128;
+// FP8 token: 512 e4m3 values, 4 fp32 scales (one per 128 values), 64 bf16 values.
+constexpr int kMlaFp8TokenBytes = 656;
 // The list is cut into pieces so that about this many workgroups run; fixed so
 // that the workspace size depends on the shape only.
 constexpr int kMlaPlanCus = 256;
@@ -23,12 +25,13 @@ constexpr int kMlaPlanCus = 256;
 int mla_workspace_bytes(int32_t batch, int32_t num_qo_heads, int32_t d_qk, int32_t d_v,
                         int32_t topk, size_t* bytes, std::string* err);
 
+// kv_pool: bf16 [pool_tokens, 576], or [pool_tokens, 656] bytes when fp8_pool.
 // attn_sink: fp32 [num_qo_heads] or NULL; topk_length: int32 [batch] or NULL.
-hipError_t launch_gather_mla(const uint16_t* q, const uint16_t* kv_pool, int64_t pool_tokens,
-                             const int32_t* indices, int32_t topk, int32_t batch,
-                             int32_t num_qo_heads, float sm_scale, const float* attn_sink,
-                             const int32_t* topk_length, void* workspace, uint16_t* out,
-                             float* lse, hipStream_t stream);
+hipError_t launch_gather_mla(const uint16_t* q, const void* kv_pool, bool fp8_pool,
+                             int64_t pool_tokens, const int32_t* indices, int32_t topk,
+                             int32_t batch, int32_t num_qo_heads, float sm_scale,
+                             const float* attn_sink, const int32_t* topk_length, void* workspace,
+                             uint16_t* out, float* lse, hipStream_t stream);
 
 }  // namespace pkv
 

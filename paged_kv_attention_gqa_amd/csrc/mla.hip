@@ -1,4 +1,5 @@
-// Index-gather latent-attention decode for gfx950 (MI355X).
+// Index-gather latent-attention decode for gfx950 (MI355X), over a bf16 pool
+// or a pool of 656-byte FP8 tokens.
 //
 // What is computed follows the FlagGems flash_mla_with_kvcache page
 // (_sparse_decode_kernel, bf16 mode): for row b every list entry
@@ -51,6 +52,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTileTok = 32;
 constexpr int kUnitsPerRow = kMlaDqk / 8;          // 72 units of 16 bytes
@@ -70,44 +72,107 @@ __device__ __forceinline__ uint16_t bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
+// Two floats rounded to bf16 (nearest, ties to even), first in the low half.
+__device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
+  return static_cast<uint32_t>(bf16_bits(a)) | (static_cast<uint32_t>(bf16_bits(b)) << 16);
+}
+
 // Thread t stages tile row t / 16: 16-byte units (t % 16) + 16 u, u = 0..4
 // (the last only for t % 16 < 8), so sixteen consecutive lanes read 256
 // contiguous bytes of one row and every thread needs one list entry per tile.
 constexpr int kThreadsPerRow = kThreads / kTileTok;   // 16
 constexpr int kLoadsPerThread = (kUnitsPerRow + kThreadsPerRow - 1) / kThreadsPerRow;   // 5
 
-struct Staged {
+// Row staging of the bf16 pool (576 bf16 = 72 units of 16 bytes per row).
+struct StagedBf16 {
   u32x4 v[kLoadsPerThread];
   bool valid;
+
+  __device__ __forceinline__ static bool has_unit(int u) {
+    return u * kThreadsPerRow + static_cast<int>(threadIdx.x % kThreadsPerRow) < kUnitsPerRow;
+  }
+
+  __device__ __forceinline__ void load(int32_t id, int64_t pool_tokens, const void* kv) {
+    valid = id >= 0 && static_cast<int64_t>(id) < pool_tokens;
+    const uint16_t* src = static_cast<const uint16_t*>(kv) +
+                          static_cast<int64_t>(valid ? id : 0) * kMlaDqk +
+                          (threadIdx.x % kThreadsPerRow) * 8;
+#pragma unroll
+    for (int u = 0; u < kLoadsPerThread; ++u)
+      if (has_unit(u)) v[u] = *reinterpret_cast<const u32x4*>(src + u * kThreadsPerRow * 8);
+  }
+
+  // A masked row is stored as zeros, so its (zero-weight) V never meets a NaN.
+  __device__ __forceinline__ void store(uint16_t* buf, uint8_t* vflag) const {
+    const int row = threadIdx.x / kThreadsPerRow;
+    uint16_t* dst = buf + row * kRowU16 + (threadIdx.x % kThreadsPerRow) * 8;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int u = 0; u < kLoadsPerThread; ++u)
+      if (has_unit(u)) *reinterpret_cast<u32x4*>(dst + u * kThreadsPerRow * 8) = valid ? v[u] : zero;
+    if (threadIdx.x % kThreadsPerRow == 0) vflag[row] = valid ? 1 : 0;
+  }
+};
+
+// Row staging of the FP8 pool: 656-byte tokens, e4m3 values [0, 512), four
+// fp32 scales [512, 528) (scale k for values 128k .. 128k+127), 64 bf16 values
+// [528, 656). Thread j of a row loads the e4m3 units j and j + 16 (values
+// 16j and 256 + 16j, +16), the scale unit, and for j < 8 the bf16 unit j; at
+// the store it multiplies each value by its scale in fp32 and rounds to bf16,
+// so the LDS tile has the same 576-bf16 rows as the bf16 pool.
+struct StagedFp8 {
+  u32x4 codes[2];
+  u32x4 scales;
+  u32x4 tail;
+  bool valid;
+
+  __device__ __forceinline__ void load(int32_t id, int64_t pool_tokens, const void* kv) {
+    valid = id >= 0 && static_cast<int64_t>(id) < pool_tokens;
+    const int j = threadIdx.x % kThreadsPerRow;
+    const uint8_t* src = static_cast<const uint8_t*>(kv) +
+                         static_cast<int64_t>(valid ? id : 0) * kMlaFp8TokenBytes;
+    codes[0] = *reinterpret_cast<const u32x4*>(src + 16 * j);
+    codes[1] = *reinterpret_cast<const u32x4*>(src + 256 + 16 * j);
+    scales = *reinterpret_cast<const u32x4*>(src + 512);
+    if (j < 8) tail = *reinterpret_cast<const u32x4*>(src + 528 + 16 * j);
+  }
+
+  __device__ __forceinline__ void store(uint16_t* buf, uint8_t* vflag) const {
+    const int row = threadIdx.x / kThreadsPerRow;
+    const int j = threadIdx.x % kThreadsPerRow;
+    uint16_t* dst = buf + row * kRowU16;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      // values 256u + 16j .. +16 lie in the 128-value block 2u + j / 8
+      const float sc = __builtin_bit_cast(float, j < 8 ? scales[2 * u] : scales[2 * u + 1]);
+      uint32_t packed[8];
+#pragma unroll
+      for (int wd = 0; wd < 4; ++wd) {
+        const int word = static_cast<int>(codes[u][wd]);
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);   // bytes 0, 1
+        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);    // bytes 2, 3
+        packed[2 * wd] = bf16_pair(lo[0] * sc, lo[1] * sc);
+        packed[2 * wd + 1] = bf16_pair(hi[0] * sc, hi[1] * sc);
+      }
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      const u32x4 a = {packed[0], packed[1], packed[2], packed[3]};
+      const u32x4 b = {packed[4], packed[5], packed[6], packed[7]};
+      uint16_t* d = dst + 256 * u + 16 * j;
+      *reinterpret_cast<u32x4*>(d) = valid ? a : zero;
+      *reinterpret_cast<u32x4*>(d + 8) = valid ? b : zero;
+    }
+    if (j < 8) {
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(dst + 512 + 8 * j) = valid ? tail : zero;
+    }
+    if (j == 0) vflag[row] = valid ? 1 : 0;
+  }
 };
 
 // Entry of this thread's row in the tile starting at t0 (-1 past the piece).
 __device__ __forceinline__ int32_t tile_entry(const int32_t* __restrict__ idx, int t0, int n) {
   const int tok = t0 + static_cast<int>(threadIdx.x) / kThreadsPerRow;
   return tok < n ? idx[tok] : -1;
-}
-
-__device__ __forceinline__ bool has_unit(int u) {
-  return u * kThreadsPerRow + static_cast<int>(threadIdx.x % kThreadsPerRow) < kUnitsPerRow;
-}
-
-__device__ __forceinline__ void load_tile(Staged& s, int32_t id, int64_t pool_tokens,
-                                          const uint16_t* __restrict__ kv) {
-  s.valid = id >= 0 && static_cast<int64_t>(id) < pool_tokens;
-  const uint16_t* src = kv + static_cast<int64_t>(s.valid ? id : 0) * kMlaDqk +
-                        (threadIdx.x % kThreadsPerRow) * 8;
-#pragma unroll
-  for (int u = 0; u < kLoadsPerThread; ++u)
-    if (has_unit(u)) s.v[u] = *reinterpret_cast<const u32x4*>(src + u * kThreadsPerRow * 8);
-}
-
-__device__ __forceinline__ void store_tile(const Staged& s, uint16_t* buf, uint8_t* vflag) {
-  const int row = threadIdx.x / kThreadsPerRow;
-  uint16_t* dst = buf + row * kRowU16 + (threadIdx.x % kThreadsPerRow) * 8;
-#pragma unroll
-  for (int u = 0; u < kLoadsPerThread; ++u)
-    if (has_unit(u)) *reinterpret_cast<u32x4*>(dst + u * kThreadsPerRow * 8) = s.v[u];
-  if (threadIdx.x % kThreadsPerRow == 0) vflag[row] = s.valid ? 1 : 0;
 }
 
 struct State {
@@ -195,8 +260,9 @@ __device__ __forceinline__ void softmax_pv(const uint16_t* buf, const uint8_t* v
 
 // grid: (pieces, head blocks, batch). Each workgroup decodes list entries
 // [piece * per_piece, +per_piece) of row b for heads [64 hb, 64 hb + 64).
+template <typename Staged>
 __global__ __launch_bounds__(kThreads) void mla_partial_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, int64_t pool_tokens,
+    const uint16_t* __restrict__ q, const void* __restrict__ kv, int64_t pool_tokens,
     const int32_t* __restrict__ indices, int topk, int num_qo_heads, int per_piece,
     float scale_log2, const float* __restrict__ attn_sink, const int32_t* __restrict__ topk_length,
     uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
@@ -242,8 +308,8 @@ __global__ __launch_bounds__(kThreads) void mla_partial_kernel(
   // masked) so that every load is unconditional.
   const int n_tiles = n > 0 ? (n + kTileTok - 1) / kTileTok : 0;
   Staged sa, sb;
-  load_tile(sa, tile_entry(idx, 0, n), pool_tokens, kv);
-  load_tile(sb, tile_entry(idx, kTileTok, n), pool_tokens, kv);
+  sa.load(tile_entry(idx, 0, n), pool_tokens, kv);
+  sb.load(tile_entry(idx, kTileTok, n), pool_tokens, kv);
   int32_t id_next = tile_entry(idx, 2 * kTileTok, n);
   for (int t = 0; t < n_tiles; t += 2) {
 #pragma unroll
@@ -252,8 +318,8 @@ __global__ __launch_bounds__(kThreads) void mla_partial_kernel(
       Staged& cur = k == 0 ? sa : sb;
       uint16_t* buf = lds + k * kBufU16;
       const int32_t id_after = tile_entry(idx, (t + k + 3) * kTileTok, n);
-      store_tile(cur, buf, vflag[k]);
-      load_tile(cur, id_next, pool_tokens, kv);   // tile t + k + 2
+      cur.store(buf, vflag[k]);
+      cur.load(id_next, pool_tokens, kv);   // tile t + k + 2
       id_next = id_after;
       __syncthreads();   // tile t+k is in LDS; every wave is done with this buffer's last tile
       f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
@@ -362,11 +428,11 @@ int mla_workspace_bytes(int32_t batch, int32_t num_qo_heads, int32_t d_qk, int32
   return 0;
 }
 
-hipError_t launch_gather_mla(const uint16_t* q, const uint16_t* kv_pool, int64_t pool_tokens,
-                             const int32_t* indices, int32_t topk, int32_t batch,
-                             int32_t num_qo_heads, float sm_scale, const float* attn_sink,
-                             const int32_t* topk_length, void* workspace, uint16_t* out,
-                             float* lse, hipStream_t stream) {
+hipError_t launch_gather_mla(const uint16_t* q, const void* kv_pool, bool fp8_pool,
+                             int64_t pool_tokens, const int32_t* indices, int32_t topk,
+                             int32_t batch, int32_t num_qo_heads, float sm_scale,
+                             const float* attn_sink, const int32_t* topk_length, void* workspace,
+                             uint16_t* out, float* lse, hipStream_t stream) {
   if (batch == 0) return hipSuccess;
   const int pieces = mla_pieces(batch, num_qo_heads, topk, kMlaPlanCus);
   const int per_piece = topk > 0 ? ((topk + pieces - 1) / pieces + kTileTok - 1) / kTileTok * kTileTok : 0;
@@ -374,9 +440,15 @@ hipError_t launch_gather_mla(const uint16_t* q, const uint16_t* kv_pool, int64_t
   float* part_o = static_cast<float*>(workspace);
   float* part_lse = pieces > 1 ? part_o + static_cast<size_t>(batch) * num_qo_heads * pieces * kMlaDv : nullptr;
   const float scale_log2 = sm_scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(mla_partial_kernel, dim3(pieces, hblocks, batch), dim3(kThreads), 0, stream, q,
-                     kv_pool, pool_tokens, indices, topk, num_qo_heads, per_piece, scale_log2,
-                     attn_sink, topk_length, out, lse, part_o, part_lse);
+  if (fp8_pool) {
+    hipLaunchKernelGGL(mla_partial_kernel<StagedFp8>, dim3(pieces, hblocks, batch), dim3(kThreads),
+                       0, stream, q, kv_pool, pool_tokens, indices, topk, num_qo_heads, per_piece,
+                       scale_log2, attn_sink, topk_length, out, lse, part_o, part_lse);
+  } else {
+    hipLaunchKernelGGL(mla_partial_kernel<StagedBf16>, dim3(pieces, hblocks, batch), dim3(kThreads),
+                       0, stream, q, kv_pool, pool_tokens, indices, topk, num_qo_heads, per_piece,
+                       scale_log2, attn_sink, topk_length, out, lse, part_o, part_lse);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pieces == 1) return e;
   hipLaunchKernelGGL(mla_merge_kernel, dim3(batch * num_qo_heads), dim3(kMlaDv / 4), 0, stream,

@@ -38,7 +38,7 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_symbols()
-    assert len(names) == 14
+    assert len(names) == 15
     for name in names:
         assert hasattr(lib, name), name
         assert name in pkv.SIGNATURES, name
@@ -331,3 +331,17 @@ def test_append_checks(lib):
     assert a(vr=FAKE + 8) == E.PKV_ERR_INVALID_ARG
     assert a(slots=FAKE + 4) == E.PKV_ERR_INVALID_ARG
     assert a(pages=2 ** 62) == E.PKV_ERR_INVALID_ARG
+
+
+def test_gather_fp8_checks(lib):
+    g = lambda **o: lib.pkv_gather_mla_fp8(
+        o.get("q", FAKE), o.get("kv", FAKE), o.get("T", 65536), o.get("idx", FAKE),
+        o.get("topk", 2048), o.get("B", 32), o.get("H", 128), o.get("dqk", 576), o.get("dv", 512),
+        o.get("scale", 0.04), None, None, o.get("ws", FAKE), o.get("wsb", 1 << 30),
+        o.get("out", FAKE), o.get("lse", FAKE), 0)
+    assert g(dqk=512) == pkv.PKV_ERR_UNSUPPORTED
+    assert g(H=100) == pkv.PKV_ERR_UNSUPPORTED
+    assert g(kv=FAKE + 8) == pkv.PKV_ERR_INVALID_ARG
+    assert g(kv=0) == pkv.PKV_ERR_INVALID_ARG
+    assert g(wsb=0) == pkv.PKV_ERR_WORKSPACE_TOO_SMALL
+    assert g(B=0) == pkv.PKV_OK

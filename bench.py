@@ -57,12 +57,11 @@ def traffic_file(config: str) -> str:
 def algorithmic_decode_bytes(w, plan_flat) -> int:
     """Bytes the decode kernel must move per launch (each byte once).
 
-    Per token: 2048 B of K/V rows. Page ids: 4 B per token for a CSR list
-    (plus the 4-byte indptr entry per sequence), 4 B per page for a block
-    table. Per sequence: 8192 B of q. Per directly written sequence: 8192 B
-    bf16 out + 128 B lse. Per split segment: 16384 B fp32 partial + 128 B
-    partial LSE. Plus the plan tables: 4 B per worker offset and 16 B per
-    segment.
+    Per token: 2048 B of K/V rows. Page ids: 4 B per token for a CSR list,
+    4 B per page for a block table. Per sequence: 8192 B of q. Per directly
+    written sequence: 8192 B bf16 out + 128 B lse. Per split segment: 16384 B
+    fp32 partial + 128 B partial LSE. Plus the plan tables: one 32-byte record
+    per segment (a worker's first segment sits in its own record).
     """
     n_workers, n_segs, n_merges, n_slots = plan_flat[:4]
     segs = np.array(plan_flat[5 + n_workers:5 + n_workers + 4 * n_segs],
@@ -72,9 +71,9 @@ def algorithmic_decode_bytes(w, plan_flat) -> int:
     if hasattr(w, "block_table"):
         ids = 4 * int(w.pages_per_seq.sum())
     else:
-        ids = 4 * n + 4 * (w.batch + 1)
+        ids = 4 * n
     return (2048 * n + ids + 8192 * w.batch + direct * (8192 + 128)
-            + n_slots * (16384 + 128) + 4 * (n_workers + 1) + 16 * n_segs)
+            + n_slots * (16384 + 128) + 32 * max(n_segs, n_workers))
 
 
 def read_traffic(config: str, kernel_src: str):

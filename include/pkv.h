@@ -66,7 +66,7 @@ typedef struct pkv_plan pkv_plan;
  * kv_indptr_host: host int32 [batch + 1], non-decreasing, kv_indptr_host[0] == 0.
  * num_cus: compute units to plan for; 0 queries the current HIP device.
  * allow_split: 0 gives one worker per sequence (nothing to merge).
- * chunk_tokens: tokens per worker; 0 uses two workers per CU (fewer for a
+ * chunk_tokens: tokens per worker; 0 uses one worker per CU (fewer for a
  * batch of under 128 tokens per worker).
  */
 pkv_status pkv_workspace_size(const int32_t* kv_indptr_host, int32_t batch,

@@ -37,7 +37,7 @@ from __future__ import annotations
 
 import bisect
 
-WORKERS_PER_CU = 2
+WORKERS_PER_CU = 1
 MIN_WORKER_TOKENS = 128
 TILE = 32
 SNAP_MIN_SHARE = 64

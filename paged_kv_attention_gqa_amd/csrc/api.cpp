@@ -132,22 +132,39 @@ pkv_status make_plan(const int32_t* kv_indptr_host, int32_t batch, int32_t num_q
     const int64_t n = static_cast<int64_t>(kv_indptr_host[b + 1]) - kv_indptr_host[b];
     p->max_seq_pages = std::max<int64_t>(p->max_seq_pages, (n + page_size - 1) / page_size);
   }
+  // Uploaded tables (all records 8 int32 = 32 bytes):
+  // * worker w: (first segment's b, tok_begin, tok_end, slot, token offset of
+  //   its sequence, s_begin, s_end, 0), so a workgroup starts its first
+  //   segment after one load;
+  // * segment s: (b, tok_begin, tok_end, slot, token offset of sequence b,
+  //   0, 0, 0), so page ids are found without reading kv_indptr;
+  // * merge records (b, first_slot, n_segments, 0).
   p->tables.clear();
-  p->tables.reserve(p->part.worker_ptr.size() + 4 * (p->part.segments.size() + p->part.merges.size()));
-  p->tables.insert(p->tables.end(), p->part.worker_ptr.begin(), p->part.worker_ptr.end());
-  const size_t n_wptr = p->part.worker_ptr.size();
-  const size_t pad = (4 - n_wptr % 4) % 4;   // segments start 16-byte aligned
-  p->tables.insert(p->tables.end(), pad, 0);
+  p->tables.reserve(8 * (p->part.worker_ptr.size() + p->part.segments.size()) +
+                    4 * p->part.merges.size());
+  for (int32_t w = 0; w < p->part.n_workers; ++w) {
+    const int32_t sb = p->part.worker_ptr[static_cast<size_t>(w)];
+    const int32_t se = p->part.worker_ptr[static_cast<size_t>(w) + 1];
+    if (sb < se) {
+      const auto& sg = p->part.segments[static_cast<size_t>(sb)];
+      p->tables.insert(p->tables.end(),
+                       {sg.b, sg.tok_begin, sg.tok_end, sg.slot, kv_indptr_host[sg.b], sb, se, 0});
+    } else {
+      p->tables.insert(p->tables.end(), {0, 0, 0, -1, 0, sb, se, 0});
+    }
+  }
+  const size_t n_wrec = 8 * static_cast<size_t>(p->part.n_workers);
   for (const auto& sg : p->part.segments) {
-    p->tables.insert(p->tables.end(), {sg.b, sg.tok_begin, sg.tok_end, sg.slot});
+    p->tables.insert(p->tables.end(),
+                     {sg.b, sg.tok_begin, sg.tok_end, sg.slot, kv_indptr_host[sg.b], 0, 0, 0});
   }
   for (const auto& m : p->part.merges) {
     p->tables.insert(p->tables.end(), {m.b, m.first_slot, m.n_segments, m.pad});
   }
   const size_t slots = static_cast<size_t>(p->part.n_slots);
   p->off_wptr = 0;
-  p->off_segs = 4 * (n_wptr + pad);
-  p->off_merges = p->off_segs + 16 * p->part.segments.size();
+  p->off_segs = 4 * n_wrec;
+  p->off_merges = p->off_segs + 32 * p->part.segments.size();
   p->off_part_o = align_up(p->off_merges + 16 * p->part.merges.size());
   p->off_part_lse = align_up(p->off_part_o + slots * num_qo_heads * head_dim * sizeof(float));
   p->ws_bytes = align_up(p->off_part_lse + slots * num_qo_heads * sizeof(float));

@@ -55,6 +55,7 @@ constexpr int kTileTok = 32;            // tokens per wave per step
 constexpr int kRowU16 = kHeadDim + 8;   // LDS row of one token's V: 256 B + 16 B pad
 constexpr int kWaveLdsU16 = kTileTok * kRowU16;
 constexpr int kThreads = 64 * kHkv;
+constexpr int kPipeTiles = 2;           // register tile buffers per wave
 constexpr float kNegInf = -__builtin_huge_valf();
 
 struct Tile {
@@ -170,8 +171,8 @@ struct TokenRows;
 template <>
 struct TokenRows<false> {
   const int32_t* ids;   // page ids of the segment's tokens
-  __device__ TokenRows(const KvAddressing& a, int b, int lo)
-      : ids(a.ids + a.kv_indptr[b] + lo) {}
+  __device__ TokenRows(const KvAddressing& a, int b, int lo, int seq_offset)
+      : ids(a.ids + seq_offset + lo) {}
   __device__ __forceinline__ int32_t operator()(int j) const { return ids[j]; }
 };
 
@@ -180,7 +181,7 @@ template <>
 struct TokenRows<true> {
   const int32_t* row;   // the sequence's block-table row
   int lo, shift, mask;
-  __device__ TokenRows(const KvAddressing& a, int b, int lo_)
+  __device__ TokenRows(const KvAddressing& a, int b, int lo_, int)
       : row(a.ids + static_cast<int64_t>(b) * a.table_stride), lo(lo_), shift(a.page_shift),
         mask((1 << a.page_shift) - 1) {}
   __device__ __forceinline__ int32_t operator()(int j) const {
@@ -193,7 +194,7 @@ struct TokenRows<true> {
 // workgroup and writes either the final out/lse (slot < 0) or a partial.
 template <bool kTable>
 __device__ __forceinline__ void process_segment(
-    int b, int lo, int n, int slot, const uint16_t* __restrict__ q,
+    int b, int lo, int n, int slot, int seq_offset, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k_pool, const uint16_t* __restrict__ v_pool,
     const KvAddressing& addr, float scale_log2, uint16_t* __restrict__ out,
     float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse,
@@ -204,7 +205,7 @@ __device__ __forceinline__ void process_segment(
   const int c = lane >> 4;
   const int head = g * kGroup + r;   // a real query head only for r < kGroup
 
-  const TokenRows<kTable> ids(addr, b, lo);
+  const TokenRows<kTable> ids(addr, b, lo, seq_offset);
   const int last = n - 1;
 
   // Q as the B operand: lane (r, c) holds q[head r][32x + 8c, +8) for k-step x.
@@ -225,42 +226,51 @@ __device__ __forceinline__ void process_segment(
   st.l = 0.f;
   uint16_t* lw = lds + g * kWaveLdsU16;   // each wave owns its LDS slice
 
-  // Software pipeline over pairs of 32-token tiles with two register
-  // buffers: while one tile is computed the other is in flight. Page ids are
-  // fetched two tiles ahead and issued before the K/V loads of the tile
-  // after the one being computed, so waiting for them never waits for
-  // younger K/V loads. The loop body has no early exit and the empty asm
-  // statements keep every load group where it is written; an odd last tile is
-  // computed after the loop from the buffer the last pair prefetched into.
+  // Software pipeline over a ring of kPipeTiles register buffers: while the
+  // oldest tile is computed, the next kPipeTiles - 1 tiles are in flight.
+  // Page ids are fetched one tile ahead of the K/V loads they feed and issued
+  // before them, so waiting for ids never waits for younger K/V loads. The
+  // loop is unrolled over the ring so every buffer index is a constant, its
+  // body has no early exit, and the empty asm statements keep each load group
+  // where it is written. Loads past the segment re-read its last row; the
+  // last n_tiles % kPipeTiles tiles are computed after the loop from the
+  // buffers the final iterations loaded.
   const int n_tiles = (n + kTileTok - 1) / kTileTok;
-  const int n_pairs = n_tiles / 2;
-  int32_t pa0 = ids(min(r, last));
-  int32_t pa1 = ids(min(16 + r, last));
-  int32_t pb0 = ids(min(32 + r, last));
-  int32_t pb1 = ids(min(48 + r, last));
-  Tile ta, tb;
-  load_tile(ta, k_pool, v_pool, pa0, pa1, g, c);
-  int t0 = 0;
-  for (int pair = 0; pair < n_pairs; ++pair) {
-    asm volatile("" ::: "memory");
-    pa0 = ids(min(t0 + 64 + r, last));
-    pa1 = ids(min(t0 + 80 + r, last));
-    load_tile(tb, k_pool, v_pool, pb0, pb1, g, c);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    compute_tile(ta, t0, n, qf, scale_log2, r, c, lw, st);
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" ::: "memory");
-    pb0 = ids(min(t0 + 96 + r, last));
-    pb1 = ids(min(t0 + 112 + r, last));
-    load_tile(ta, k_pool, v_pool, pa0, pa1, g, c);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    compute_tile(tb, t0 + kTileTok, n, qf, scale_log2, r, c, lw, st);
-    __builtin_amdgcn_sched_barrier(0);
-    t0 += 2 * kTileTok;
+  const int n_rounds = n_tiles / kPipeTiles;
+  Tile ring[kPipeTiles];
+#pragma unroll
+  for (int k = 0; k < kPipeTiles - 1; ++k) {
+    const int32_t a0 = ids(min(kTileTok * k + r, last));
+    const int32_t a1 = ids(min(kTileTok * k + 16 + r, last));
+    load_tile(ring[k], k_pool, v_pool, a0, a1, g, c);
   }
-  if (n_tiles & 1) compute_tile(ta, t0, n, qf, scale_log2, r, c, lw, st);
+  int32_t next0 = ids(min(kTileTok * (kPipeTiles - 1) + r, last));
+  int32_t next1 = ids(min(kTileTok * (kPipeTiles - 1) + 16 + r, last));
+  int t0 = 0;
+  for (int round = 0; round < n_rounds; ++round) {
+#pragma unroll
+    for (int k = 0; k < kPipeTiles; ++k) {
+      // compute tile round * kPipeTiles + k (ring[k]); load the tile
+      // kPipeTiles - 1 later into the buffer computed last; fetch the ids of
+      // the tile after that.
+      asm volatile("" ::: "memory");
+      const int tf = t0 + kTileTok * (k + kPipeTiles);
+      const int32_t f0 = ids(min(tf + r, last));
+      const int32_t f1 = ids(min(tf + 16 + r, last));
+      load_tile(ring[(k + kPipeTiles - 1) % kPipeTiles], k_pool, v_pool, next0, next1, g, c);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      compute_tile(ring[k], t0 + kTileTok * k, n, qf, scale_log2, r, c, lw, st);
+      __builtin_amdgcn_sched_barrier(0);
+      next0 = f0;
+      next1 = f1;
+    }
+    t0 += kTileTok * kPipeTiles;
+  }
+  const int rest = n_tiles - n_rounds * kPipeTiles;
+#pragma unroll
+  for (int k = 0; k < kPipeTiles - 1; ++k)
+    if (k < rest) compute_tile(ring[k], t0 + kTileTok * k, n, qf, scale_log2, r, c, lw, st);
 
   float l_tot = st.l + __shfl_xor(st.l, 16);
   l_tot += __shfl_xor(l_tot, 32);
@@ -291,20 +301,22 @@ __device__ __forceinline__ void process_segment(
 // One workgroup per worker: it walks its segments in order.
 template <bool kTable>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_partial_kernel(
-    const int32_t* __restrict__ worker_ptr, const int32_t* __restrict__ segments,
+    const int32_t* __restrict__ workers, const int32_t* __restrict__ segments,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
     const uint16_t* __restrict__ v_pool, KvAddressing addr, float scale_log2,
     uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
     float* __restrict__ part_lse) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[kHkv * kWaveLdsU16];
-  const int s_end = worker_ptr[blockIdx.x + 1];
-  for (int s = worker_ptr[blockIdx.x]; s < s_end; ++s) {
-    const int32_t* seg = segments + 4 * s;
+  const int32_t* wrec = workers + 8 * blockIdx.x;   // first segment inline, then its range
+  const int s_begin = wrec[5];
+  const int s_end = wrec[6];
+  for (int s = s_begin; s < s_end; ++s) {
+    const int32_t* seg = s == s_begin ? wrec : segments + 8 * s;
     const int lo = seg[1];
     const int n = seg[2] - lo;
     if (n > 0)
-      process_segment<kTable>(seg[0], lo, n, seg[3], q, k_pool, v_pool, addr, scale_log2, out,
-                              lse, part_o, part_lse, lds);
+      process_segment<kTable>(seg[0], lo, n, seg[3], seg[4], q, k_pool, v_pool, addr, scale_log2,
+                              out, lse, part_o, part_lse, lds);
   }
 }
 
@@ -373,7 +385,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ 
 
 }  // namespace
 
-hipError_t launch_decode_partial(const int32_t* worker_ptr, const int32_t* segments,
+hipError_t launch_decode_partial(const int32_t* workers, const int32_t* segments,
                                  int32_t n_workers, const uint16_t* q,
                                  const uint16_t* k_pool, const uint16_t* v_pool,
                                  const KvAddressing& addr, float sm_scale_log2, uint16_t* out,
@@ -381,11 +393,11 @@ hipError_t launch_decode_partial(const int32_t* worker_ptr, const int32_t* segme
   if (n_workers <= 0) return hipSuccess;
   if (addr.kv_indptr == nullptr) {
     hipLaunchKernelGGL(decode_partial_kernel<true>, dim3(n_workers), dim3(kThreads), 0, stream,
-                       worker_ptr, segments, q, k_pool, v_pool, addr, sm_scale_log2, out, lse,
+                       workers, segments, q, k_pool, v_pool, addr, sm_scale_log2, out, lse,
                        part_o, part_lse);
   } else {
     hipLaunchKernelGGL(decode_partial_kernel<false>, dim3(n_workers), dim3(kThreads), 0, stream,
-                       worker_ptr, segments, q, k_pool, v_pool, addr, sm_scale_log2, out, lse,
+                       workers, segments, q, k_pool, v_pool, addr, sm_scale_log2, out, lse,
                        part_o, part_lse);
   }
   return hipGetLastError();

@@ -17,7 +17,8 @@ constexpr int kHeadDim = 128;
 
 // How the decode kernel finds the pool row (page * page_size + slot) of
 // token t of sequence b:
-// * CSR list (kv_indptr != NULL, page size 1): row = ids[kv_indptr[b] + t];
+// * CSR list (kv_indptr != NULL, page size 1): row = ids[kv_indptr[b] + t],
+//   with kv_indptr[b] taken from the segment record (the plan's host copy);
 // * block table (kv_indptr == NULL): row = (ids[b * table_stride + (t >> page_shift)]
 //   << page_shift) | (t & (page_size - 1)).
 struct KvAddressing {
@@ -27,9 +28,11 @@ struct KvAddressing {
   int32_t page_shift;
 };
 
-// One workgroup per worker; worker w decodes the segments
-// segments[worker_ptr[w] .. worker_ptr[w+1]), each (b, tok_begin, tok_end, slot).
-hipError_t launch_decode_partial(const int32_t* worker_ptr, const int32_t* segments,
+// One workgroup per worker; worker w decodes the segments [s_begin, s_end)
+// named by its record workers[8w .. 8w+8) = (the first segment's five fields,
+// s_begin, s_end, 0); segment records are 8 int32:
+// (b, tok_begin, tok_end, slot, kv_indptr[b], 0, 0, 0).
+hipError_t launch_decode_partial(const int32_t* workers, const int32_t* segments,
                                  int32_t n_workers, const uint16_t* q,
                                  const uint16_t* k_pool, const uint16_t* v_pool,
                                  const KvAddressing& addr, float sm_scale_log2, uint16_t* out,

@@ -22,7 +22,7 @@
 
 namespace pkv {
 
-constexpr int32_t kWorkersPerCu = 2;       // decode workgroups resident per CU
+constexpr int32_t kWorkersPerCu = 1;       // decode workgroups per CU
 constexpr int32_t kMinWorkerTokens = 128;  // fewest tokens given to one worker
 constexpr int32_t kTile = 32;              // tokens per decode tile
 constexpr int32_t kSnapMinShare = 64;      // shares at least this long get tile-aligned boundaries

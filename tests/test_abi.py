@@ -97,9 +97,8 @@ def test_workspace_size_formula(lib):
     assert st == pkv.PKV_OK
     per_worker, merges, slots = plan_ref.make_plan(ind, 256, True, 256)
     al = lambda x: -(-x // 256) * 256
-    n_wptr = len(per_worker) + 1
     segs = sum(len(s) for s in per_worker)
-    tables = 4 * (n_wptr + (-n_wptr) % 4) + 16 * (segs + len(merges))
+    tables = 32 * len(per_worker) + 32 * segs + 16 * len(merges)
     part_o = al(tables)
     part_lse = al(part_o + slots * 32 * 128 * 4)
     assert n == al(part_lse + slots * 32 * 4)

@@ -143,8 +143,11 @@ struct StagedFp8 {
     uint16_t* dst = buf + row * kRowU16;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      // values 256u + 16j .. +16 lie in the 128-value block 2u + j / 8
-      const float sc = __builtin_bit_cast(float, j < 8 ? scales[2 * u] : scales[2 * u + 1]);
+      // values 256u + 16j .. +16 lie in the 128-value block 2u + j / 8 (the
+      // element is copied out first: a bit cast applied directly to a vector
+      // element compiled as a cast of element 0)
+      const uint32_t sc_bits = j < 8 ? scales[2 * u] : scales[2 * u + 1];
+      const float sc = __builtin_bit_cast(float, sc_bits);
       uint32_t packed[8];
 #pragma unroll
       for (int wd = 0; wd < 4; ++wd) {

@@ -190,3 +190,42 @@ def test_prepared_calls_match():
         merge()
     torch.cuda.synchronize()
     check(w, oracle("edge"), (bf16_to_np(out), lse.cpu().numpy().astype(np.float64)), "prepared")
+
+
+def test_hip_graph_replay_matches_eager():
+    """run + merge captured once in a HIP graph and replayed several times, with
+    eager work and synchronisations between replays: every replay equals the
+    eager result bit for bit (the calls enqueue kernels only)."""
+    w = workload("edge")
+    dev = upload_gqa(w)
+    ws = torch.empty(pkv.pkv_workspace_size(w.kv_indptr), dtype=torch.uint8, device="cuda")
+    plan = pkv.pkv_plan_create(w.kv_indptr, workspace=ws)
+    out = torch.empty_like(dev["q"])
+    lse = torch.empty(dev["q"].shape[:2], dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    pkv.pkv_run(plan, dev["q"], dev["k"], dev["v"], dev["indptr"], dev["indices"], w.sm_scale, ws,
+                out, lse)
+    pkv.pkv_merge(plan, ws, out, lse)
+    torch.cuda.synchronize()
+    want = (bf16_to_np(out), lse.cpu().numpy().astype(np.float64))
+    check(w, oracle("edge"), want, "eager")
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        run = pkv.prepare_run(plan, dev["q"], dev["k"], dev["v"], dev["indptr"], dev["indices"],
+                              w.sm_scale, ws, out, lse, stream=s.cuda_stream)
+        merge = pkv.prepare_merge(plan, ws, out, lse, stream=s.cuda_stream)
+        with torch.cuda.graph(graph, stream=s):
+            run()
+            merge()
+    torch.cuda.synchronize()
+    for i in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(0.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = (bf16_to_np(out), lse.cpu().numpy().astype(np.float64))
+        assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1]), f"replay {i}"

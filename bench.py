@@ -48,6 +48,7 @@ WORKLOAD_TEXT = {
                  "h_q=32 h_kv=4 d=128 page_size=16",
 }
 KERNEL_SRC = os.path.join(ROOT, "paged_kv_attention_gqa_amd", "csrc", "decode.hip")
+PLAN_SRC = os.path.join(ROOT, "paged_kv_attention_gqa_amd", "csrc", "plan.cpp")
 
 
 def traffic_file(config: str) -> str:
@@ -76,10 +77,20 @@ def algorithmic_decode_bytes(w, plan_flat) -> int:
             + n_slots * (16384 + 128) + 32 * max(n_segs, n_workers))
 
 
-def read_traffic(config: str, kernel_src: str):
-    """HBM bytes per launch from the committed counter summary of this workload,
-    or None if there is none or the kernel source has changed since."""
+def sources_sha256() -> str:
+    """sha256 over the decode kernel's source and the partition rule's source,
+    the two files the counted bytes of one launch depend on."""
     import hashlib
+    h = hashlib.sha256()
+    for path in (KERNEL_SRC, PLAN_SRC):
+        h.update(open(path, "rb").read())
+    return h.hexdigest()
+
+
+def read_traffic(config: str):
+    """HBM bytes per launch from the committed counter summary of this workload,
+    or None if there is none or the kernel or the partition rule has changed
+    since."""
     path = traffic_file(config)
     if not os.path.exists(path):
         return None
@@ -88,8 +99,7 @@ def read_traffic(config: str, kernel_src: str):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             vals[k.strip()] = v.strip()
-    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
-    if vals.get("kernel_source_sha256") != sha:
+    if vals.get("sources_sha256") != sources_sha256():
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -398,7 +408,7 @@ def main():
     value = kv_bytes / (wall / args.steps) / 1e9
     alg = algorithmic_decode_bytes(w, flat)
     achieved = alg / decode_s / 1e9
-    traffic = read_traffic(args.config, KERNEL_SRC)
+    traffic = read_traffic(args.config)
 
     rec = {
         "metric": METRIC,

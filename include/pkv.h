@@ -102,8 +102,10 @@ void pkv_plan_destroy(pkv_plan* plan);
  * (b, tok_begin, tok_end, slot) with token positions relative to sequence b
  * and slot -1 for a sequence written directly, then n_merges records
  * (b, first_slot, n_segments, 0) (n_segments 0 for an empty sequence).
- * Worker w (one workgroup) owns an equal share of the batch's tokens taken in
- * kv_indices order. *needed receives the count of int32 values; dst may be
+ * Worker w (one workgroup) owns a contiguous run of the batch's tokens in
+ * kv_indices order; the runs are balanced by cost (whole 32-token tiles plus
+ * 32 tokens' worth for each segment), so a worker may hold fewer tokens when
+ * it holds more segments. *needed receives the count of int32 values; dst may be
  * NULL to query it. Fails with PKV_ERR_INVALID_ARG when n_int32 is smaller
  * than that count.
  */

@@ -9,15 +9,21 @@ keys into contiguous pieces with no empty piece and merging the partials by
 LSE ([QSA page] ``qsa_sparse_paged_attention`` and its split-K kernel). The
 exact rule is this library's own and is stated here once:
 
-* The batch's ``N = kv_indptr[B]`` tokens, in ``kv_indices`` order, go to
-  ``W`` workers; worker ``w`` owns positions ``[s_w, s_(w+1))`` with
-  ``s_w = w*N//W``. When ``N//W >= SNAP_MIN_SHARE``, every interior ``s_w`` is
-  moved to the nearest (ties: lower) position ``indptr[b] + TILE*k`` inside
-  the sequence ``b`` that holds it (``indptr[b] <= s_w < indptr[b+1]``),
-  capped at ``indptr[b+1]``, so that a sequence's pieces are whole tiles.
-  ``W = ceil(N / chunk_tokens)`` when ``chunk_tokens > 0``, else
-  ``min(num_cus * WORKERS_PER_CU, ceil(N / MIN_WORKER_TOKENS))``; ``W = 0``
-  when ``N = 0``.
+* The batch's ``N = kv_indptr[B]`` tokens go, sequence by sequence in order,
+  to at most ``W`` workers, ``W = ceil(N / chunk_tokens)`` when
+  ``chunk_tokens > 0``, else ``min(num_cus * WORKERS_PER_CU,
+  ceil(N / MIN_WORKER_TOKENS))``; no workers when ``N = 0``. A piece of ``n``
+  tokens of one sequence costs ``ceil(n / TILE) * TILE + SEGMENT_COST`` (its
+  tiles, plus one tile's worth for starting a segment). Workers are filled
+  greedily with a cost budget ``C``: the rest of the current sequence goes to
+  the current worker whole if its cost fits in what the worker has left;
+  otherwise the worker takes the largest whole number of tiles whose cost
+  fits (possibly none) and the next worker continues. ``C`` is the smallest
+  budget from ``TILE + SEGMENT_COST`` up that needs at most ``W`` workers,
+  found by bisection (``lo, hi = TILE + SEGMENT_COST, max(lo, sum of the
+  whole sequences' costs)``; while ``lo < hi``: ``mid = (lo + hi) // 2``,
+  ``hi = mid`` if ``mid`` needs at most ``W`` workers, else ``lo = mid + 1``).
+  The plan has as many workers as that fill uses, possibly fewer than ``W``.
 * Each non-empty sequence becomes one segment per worker it overlaps:
   ``(b, lo, hi, slot)`` with ``lo, hi`` relative to the sequence. A sequence
   inside one worker has ``slot = -1`` (written directly); a sequence cut into
@@ -35,23 +41,60 @@ merge records (4 int32 each).
 
 from __future__ import annotations
 
-import bisect
-
 WORKERS_PER_CU = 1
 MIN_WORKER_TOKENS = 128
 TILE = 32
-SNAP_MIN_SHARE = 64
+SEGMENT_COST = 32
 
 
 def _cdiv(a: int, b: int) -> int:
     return -(-a // b)
 
 
-def round_half_down(x: float) -> int:
-    """Nearest integer, halves rounded down (x >= 0)."""
-    import math
-    f = math.floor(x)
-    return f + 1 if x - f > 0.5 else f
+def piece_cost(n: int) -> int:
+    return _cdiv(n, TILE) * TILE + SEGMENT_COST
+
+
+def fill(lengths, budget: int, record: bool = True):
+    """Greedy fill of the sequences' tokens into workers of cost ``budget``.
+
+    Returns ``(workers used, pieces (w, b, lo, hi) in order)``, or
+    ``(None, [])`` when the budget is below one tile plus a segment. The
+    pieces are only listed when ``record`` is set."""
+    full = (budget - SEGMENT_COST) // TILE * TILE   # what a fresh worker takes of a longer rest
+    if full <= 0:
+        return None, []
+    pieces = []
+    w, room, used = 0, budget, 0
+    for b, n in enumerate(lengths):
+        pos = 0
+        while pos < n:
+            rest = n - pos
+            if room == budget and rest > full:
+                # fresh workers, each taking `full` tokens, until the rest fits one
+                k = (rest - 1) // full
+                if record:
+                    pieces.extend((w + i, b, pos + i * full, pos + (i + 1) * full)
+                                  for i in range(k))
+                w += k
+                pos += k * full
+                used = w
+                continue
+            if piece_cost(rest) <= room:
+                if record:
+                    pieces.append((w, b, pos, n))
+                room -= piece_cost(rest)
+                used = w + 1
+                pos = n
+                continue
+            take = max(0, (room - SEGMENT_COST) // TILE * TILE)
+            if take:
+                if record:
+                    pieces.append((w, b, pos, pos + take))
+                used = w + 1
+                pos += take
+            w, room = w + 1, budget
+    return used, pieces
 
 
 def make_plan(kv_indptr, num_cus: int, allow_split: bool = True, chunk_tokens: int = 0):
@@ -59,48 +102,50 @@ def make_plan(kv_indptr, num_cus: int, allow_split: bool = True, chunk_tokens: i
     indptr = [int(x) for x in kv_indptr]
     batch = len(indptr) - 1
     total = indptr[-1]
+    lengths = [indptr[b + 1] - indptr[b] for b in range(batch)]
     merges = []
     if not allow_split:
-        seqs = [b for b in range(batch) if indptr[b + 1] > indptr[b]]
-        merges = [(b, 0, 0, 0) for b in range(batch) if indptr[b + 1] == indptr[b]]
-        seqs.sort(key=lambda b: (-(indptr[b + 1] - indptr[b]), b))
-        return [[(b, 0, indptr[b + 1] - indptr[b], -1)] for b in seqs], merges, 0
+        seqs = [b for b in range(batch) if lengths[b] > 0]
+        merges = [(b, 0, 0, 0) for b in range(batch) if lengths[b] == 0]
+        seqs.sort(key=lambda b: (-lengths[b], b))
+        return [[(b, 0, lengths[b], -1)] for b in seqs], merges, 0
 
     if total == 0:
-        workers = 0
+        limit = 0
     elif chunk_tokens > 0:
-        workers = _cdiv(total, chunk_tokens)
+        limit = _cdiv(total, chunk_tokens)
     else:
-        workers = min(num_cus * WORKERS_PER_CU, _cdiv(total, MIN_WORKER_TOKENS))
-    bounds = [w * total // workers for w in range(workers)] + [total] if workers else [0]
-    if workers > 1 and total // workers >= SNAP_MIN_SHARE:
-        for w in range(1, workers):
-            pos = bounds[w]
-            b = bisect.bisect_right(indptr, pos) - 1          # indptr[b] <= pos < indptr[b+1]
-            k = round_half_down((pos - indptr[b]) / TILE)
-            bounds[w] = min(indptr[b] + TILE * k, indptr[b + 1])
-    per_worker = [[] for _ in range(workers)]
+        limit = min(num_cus * WORKERS_PER_CU, _cdiv(total, MIN_WORKER_TOKENS))
+    pieces = []
+    if limit:
+        lo = TILE + SEGMENT_COST
+        hi = max(lo, sum(piece_cost(n) for n in lengths if n))
+        while lo < hi:
+            mid = (lo + hi) // 2
+            used, _ = fill(lengths, mid, record=False)
+            if used is not None and used <= limit:
+                hi = mid
+            else:
+                lo = mid + 1
+        _, pieces = fill(lengths, lo)
+    per_worker = [[] for _ in range(pieces[-1][0] + 1 if pieces else 0)]
+    by_seq = {}
+    for w, b, lo_, hi_ in pieces:
+        by_seq.setdefault(b, []).append((w, lo_, hi_))
     slot = 0
     for b in range(batch):
-        lo, hi = indptr[b], indptr[b + 1]
-        if lo == hi:
+        if lengths[b] == 0:
             merges.append((b, 0, 0, 0))
             continue
-        pieces = []
-        w = bisect.bisect_right(bounds, lo) - 1          # worker holding position lo
-        while w < workers and bounds[w] < hi:
-            a, e = max(lo, bounds[w]), min(hi, bounds[w + 1])
-            if e > a:
-                pieces.append((w, a - lo, e - lo))
-            w += 1
-        if len(pieces) == 1:
-            w, a, e = pieces[0]
+        parts = by_seq[b]
+        if len(parts) == 1:
+            w, a, e = parts[0]
             per_worker[w].append((b, a, e, -1))
         else:
-            for j, (w, a, e) in enumerate(pieces):
+            for j, (w, a, e) in enumerate(parts):
                 per_worker[w].append((b, a, e, slot + j))
-            merges.append((b, slot, len(pieces), 0))
-            slot += len(pieces)
+            merges.append((b, slot, len(parts), 0))
+            slot += len(parts)
     return per_worker, merges, slot
 
 

@@ -14,7 +14,7 @@
 // kernel below uses; page sizes are powers of two.
 //
 // Design (gfx950, wave64):
-// * One workgroup per worker of the plan: an equal share of the batch's tokens,
+// * One workgroup per worker of the plan: a cost-balanced run of the batch's tokens,
 //   as a list of (sequence, token range) segments. Wave w handles KV head w
 //   and its 8 query heads and walks each segment in tiles of 32 tokens.
 // * Both contractions run on v_mfma_f32_16x16x32_bf16, the 8 query heads

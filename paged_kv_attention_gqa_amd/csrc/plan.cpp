@@ -9,6 +9,65 @@ namespace {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Cost of decoding n tokens of one sequence as one segment, in tokens: its
+// tiles plus the fixed price of starting a segment.
+int64_t piece_cost(int64_t n) { return cdiv(n, kTile) * kTile + kSegmentCost; }
+
+struct Piece {
+  int64_t w;
+  int32_t b, lo, hi;
+};
+
+// Fills workers of cost `budget` with the sequences in order: the rest of a
+// sequence goes whole to the current worker if it fits, else the worker takes
+// the whole tiles that fit and the next worker continues. Returns the number
+// of workers used (-1 if the budget cannot hold one tile and a segment) and,
+// if `pieces` is given, the pieces in order.
+int64_t greedy_fill(const int32_t* kv_indptr, int32_t batch, int64_t budget,
+                    std::vector<Piece>* pieces) {
+  const int64_t full = (budget - kSegmentCost) / kTile * kTile;   // budget >= 0
+  if (full <= 0) return -1;
+  if (pieces) pieces->clear();
+  int64_t w = 0, room = budget, used = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t n = kv_indptr[b + 1] - kv_indptr[b];
+    int64_t pos = 0;
+    while (pos < n) {
+      const int64_t rest = n - pos;
+      if (room == budget && rest > full) {
+        // fresh workers taking `full` tokens each until the rest fits one
+        const int64_t k = (rest - 1) / full;
+        if (pieces) {
+          for (int64_t x = 0; x < k; ++x)
+            pieces->push_back({w + x, b, static_cast<int32_t>(pos + x * full),
+                               static_cast<int32_t>(pos + (x + 1) * full)});
+        }
+        w += k;
+        pos += k * full;
+        used = w;
+        continue;
+      }
+      if (piece_cost(rest) <= room) {
+        if (pieces) pieces->push_back({w, b, static_cast<int32_t>(pos), static_cast<int32_t>(n)});
+        room -= piece_cost(rest);
+        used = w + 1;
+        pos = n;
+        continue;
+      }
+      const int64_t take = room > kSegmentCost ? (room - kSegmentCost) / kTile * kTile : 0;
+      if (take > 0) {
+        if (pieces)
+          pieces->push_back({w, b, static_cast<int32_t>(pos), static_cast<int32_t>(pos + take)});
+        used = w + 1;
+        pos += take;
+      }
+      ++w;
+      room = budget;
+    }
+  }
+  return used;
+}
+
 }  // namespace
 
 bool build_partition(const int32_t* kv_indptr, int32_t batch, int32_t num_cus,
@@ -50,64 +109,55 @@ bool build_partition(const int32_t* kv_indptr, int32_t batch, int32_t num_cus,
     return true;
   }
 
-  int64_t workers;
+  int64_t limit;
   if (total == 0) {
-    workers = 0;
+    limit = 0;
   } else if (chunk_tokens > 0) {
-    workers = cdiv(total, chunk_tokens);
+    limit = cdiv(total, chunk_tokens);
   } else {
-    workers = std::min<int64_t>(int64_t(num_cus) * kWorkersPerCu, cdiv(total, kMinWorkerTokens));
+    limit = std::min<int64_t>(int64_t(num_cus) * kWorkersPerCu, cdiv(total, kMinWorkerTokens));
+  }
+  std::vector<Piece> pieces;
+  int64_t workers = 0;
+  if (limit > 0) {
+    // Smallest budget whose greedy fill needs at most `limit` workers; the
+    // sum of the whole sequences' costs always fits one worker.
+    int64_t lo = kTile + kSegmentCost, hi = 0;
+    for (int32_t b = 0; b < batch; ++b) {
+      const int64_t n = kv_indptr[b + 1] - kv_indptr[b];
+      if (n > 0) hi += piece_cost(n);
+    }
+    hi = std::max(hi, lo);
+    while (lo < hi) {
+      const int64_t mid = lo + (hi - lo) / 2;
+      const int64_t used = greedy_fill(kv_indptr, batch, mid, nullptr);
+      if (used >= 0 && used <= limit) hi = mid;
+      else lo = mid + 1;
+    }
+    workers = greedy_fill(kv_indptr, batch, lo, &pieces);
   }
   p.n_workers = static_cast<int32_t>(workers);
-  // Worker w owns the tokens [start[w], start[w+1]), start[w] = w*total/workers,
-  // each interior boundary moved (by at most 16 tokens) to the nearest
-  // position that is a multiple of kTile tokens into its sequence, or to the
-  // sequence's end, so that pieces of a sequence are whole tiles. Shares under
-  // kSnapMinShare tokens are not moved.
-  std::vector<int64_t> starts(static_cast<size_t>(workers) + 1);
-  for (int64_t w = 0; w <= workers; ++w) starts[static_cast<size_t>(w)] = workers ? w * total / workers : 0;
-  if (workers > 1 && total / workers >= kSnapMinShare) {
-    for (int64_t w = 1; w < workers; ++w) {
-      const int64_t pos = starts[static_cast<size_t>(w)];
-      // sequence holding pos: last b with kv_indptr[b] <= pos
-      const int32_t b = static_cast<int32_t>(
-          std::upper_bound(kv_indptr, kv_indptr + batch + 1, static_cast<int32_t>(pos)) - kv_indptr - 1);
-      const int64_t off = pos - kv_indptr[b];
-      int64_t snapped = kv_indptr[b] + kTile * ((off + kTile / 2 - 1) / kTile);
-      snapped = std::min<int64_t>(snapped, kv_indptr[b + 1]);
-      starts[static_cast<size_t>(w)] = snapped;
-    }
-  }
-  auto start = [&](int64_t w) { return starts[static_cast<size_t>(w)]; };
 
   std::vector<std::vector<Segment>> per_worker(static_cast<size_t>(workers));
   int32_t slot = 0;
+  size_t i = 0;
   for (int32_t b = 0; b < batch; ++b) {
-    const int64_t lo = kv_indptr[b], hi = kv_indptr[b + 1];
-    if (hi == lo) {
+    if (kv_indptr[b + 1] == kv_indptr[b]) {
       p.merges.push_back({b, 0, 0, 0});
       continue;
     }
-    // first worker whose range contains lo: largest w with start(w) <= lo
-    int64_t w = std::min<int64_t>(workers - 1, (lo * workers) / total);
-    while (w > 0 && start(w) > lo) --w;
-    while (w + 1 < workers && start(w + 1) <= lo) ++w;
-    const bool single = hi <= start(w + 1);
-    int32_t k = 0;
-    for (int64_t pos = lo; pos < hi; ++w) {
-      const int64_t end = std::min<int64_t>(hi, start(w + 1));
-      if (end > pos) {
-        per_worker[static_cast<size_t>(w)].push_back(
-            {b, static_cast<int32_t>(pos - lo), static_cast<int32_t>(end - lo),
-             single ? -1 : slot + k});
-        ++k;
-      }
-      pos = end;
+    size_t j = i;
+    while (j < pieces.size() && pieces[j].b == b) ++j;
+    const int32_t k = static_cast<int32_t>(j - i);
+    for (size_t x = i; x < j; ++x) {
+      per_worker[static_cast<size_t>(pieces[x].w)].push_back(
+          {b, pieces[x].lo, pieces[x].hi, k == 1 ? -1 : slot + static_cast<int32_t>(x - i)});
     }
-    if (!single) {
+    if (k > 1) {
       p.merges.push_back({b, slot, k, 0});
       slot += k;
     }
+    i = j;
   }
   p.n_slots = slot;
   p.worker_ptr.push_back(0);

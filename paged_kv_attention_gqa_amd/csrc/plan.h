@@ -1,10 +1,15 @@
 // Split-KV work partition for paged decode (host only, no HIP).
 //
-// The batch's tokens, taken in kv_indices order, are cut into equal
-// contiguous ranges, one per worker (one workgroup of the decode kernel); each
-// cut inside a sequence is moved to a whole number of 32-token tiles into it.
-// A worker's range is a list of segments (b, tok_begin, tok_end, slot), one
-// per sequence it touches, with token positions relative to the sequence. A
+// The batch's sequences, in order, are cut into contiguous pieces and dealt
+// to workers (one workgroup of the decode kernel each) so that every worker
+// gets about the same cost: a piece of n tokens costs its whole 32-token
+// tiles plus kSegmentCost tokens for starting a segment (measured: a
+// workgroup spends about one tile's time on each extra segment). Workers are
+// filled greedily under a cost budget, the smallest budget that needs at most
+// the allowed number of workers (found by bisection); cuts inside a sequence
+// fall on whole tiles. A worker's share is a list of segments
+// (b, tok_begin, tok_end, slot), one per sequence it touches, with token
+// positions relative to the sequence. A
 // sequence that lies inside one worker is written directly (slot = -1); a
 // sequence cut across workers leaves one normalised fp32 partial per segment
 // in consecutive workspace slots, combined by a merge record
@@ -25,7 +30,7 @@ namespace pkv {
 constexpr int32_t kWorkersPerCu = 1;       // decode workgroups per CU
 constexpr int32_t kMinWorkerTokens = 128;  // fewest tokens given to one worker
 constexpr int32_t kTile = 32;              // tokens per decode tile
-constexpr int32_t kSnapMinShare = 64;      // shares at least this long get tile-aligned boundaries
+constexpr int32_t kSegmentCost = 32;       // tokens' worth of time to start a segment
 
 struct Segment {
   int32_t b, tok_begin, tok_end, slot;
@@ -45,8 +50,9 @@ struct Partition {
 
 // Checks kv_indptr (starts at 0, non-decreasing) and builds the partition.
 // allow_split = false gives one worker per sequence. chunk_tokens > 0 sets
-// the tokens per worker; 0 chooses num_cus * kWorkersPerCu workers (fewer
-// when the batch has under kMinWorkerTokens tokens per worker). Returns false
+// the most workers to ceil(N / chunk_tokens); 0 to num_cus * kWorkersPerCu
+// (fewer when the batch has under kMinWorkerTokens tokens per worker); the
+// fill may use fewer. Returns false
 // with a message in *err on bad input.
 bool build_partition(const int32_t* kv_indptr, int32_t batch, int32_t num_cus,
                      bool allow_split, int32_t chunk_tokens, Partition* out, std::string* err);

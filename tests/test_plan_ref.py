@@ -37,16 +37,23 @@ def _check(indptr, num_cus, allow_split, chunk_tokens):
     assert sorted(seen_slots) == list(range(slots))
     assert [m[0] for m in merges] == sorted(m[0] for m in merges)
     if allow_split and total:
-        sizes = [sum(hi - lo for _, lo, hi, _ in segs) for segs in per_worker]
-        snapped = len(per_worker) > 1 and total // len(per_worker) >= plan_ref.SNAP_MIN_SHARE
-        assert max(sizes) - min(sizes) <= (1 + 4 * (plan_ref.TILE // 2) if snapped else 1)
-        if snapped:   # interior pieces of a sequence are whole tiles
-            for segs in per_worker:
-                for b, lo, hi, slot in segs:
-                    if slot >= 0 and hi < int(indptr[b + 1] - indptr[b]):
-                        assert (hi - lo) % plan_ref.TILE == 0 or lo % plan_ref.TILE != 0
-        if chunk_tokens == 0:
-            assert len(per_worker) <= num_cus * plan_ref.WORKERS_PER_CU
+        tile, seg = plan_ref.TILE, plan_ref.SEGMENT_COST
+        for segs in per_worker:
+            for b, lo, hi, slot in segs:
+                assert lo % tile == 0                    # cuts fall on whole tiles
+        costs = [sum(plan_ref.piece_cost(hi - lo) for _, lo, hi, _ in segs) for segs in per_worker]
+        budget = max(costs)
+        # every worker but the last was closed with less room left than one
+        # tile plus a segment
+        assert all(c > budget - tile - seg for c in costs[:-1])
+        limit = (-(-total // chunk_tokens) if chunk_tokens > 0
+                 else min(num_cus * plan_ref.WORKERS_PER_CU, -(-total // plan_ref.MIN_WORKER_TOKENS)))
+        assert len(per_worker) <= limit
+        # the budget is the smallest that fits: one less needs more workers
+        if budget > tile + seg:
+            used, _ = plan_ref.fill([int(indptr[b + 1] - indptr[b]) for b in range(batch)],
+                                    budget - 1, record=False)
+            assert used is None or used > limit
     if not allow_split:
         assert slots == 0 and all(len(s) == 1 for s in per_worker)
 
@@ -69,23 +76,30 @@ def test_plan_no_split_is_one_worker_per_sequence():
 
 
 def test_plan_hand_example():
-    # 610 tokens over ceil(610/256) = 3 workers: cuts at 203 and 406, moved to
-    # the nearest multiple of 32 into sequence 0: 192 (203 = 6*32 + 11) and 416
+    # 610 tokens, at most ceil(610/256) = 3 workers. Costs: sequence 0 (600
+    # tokens) 608 + 32, sequence 2 (10 tokens) 32 + 32. Budget 256: workers 0
+    # and 1 take (256 - 32) // 32 * 32 = 224 tokens each, worker 2 the last 152
+    # (160 + 32) and sequence 2 (64): 256. Budget 255 takes 192 a worker and
+    # would need a fourth worker for the rest.
     per_worker, merges, slots = plan_ref.make_plan([0, 600, 600, 610], 1, chunk_tokens=256)
-    assert per_worker == [[(0, 0, 192, 0)], [(0, 192, 416, 1)], [(0, 416, 600, 2), (2, 0, 10, -1)]]
+    assert per_worker == [[(0, 0, 224, 0)], [(0, 224, 448, 1)], [(0, 448, 600, 2), (2, 0, 10, -1)]]
     assert merges == [(0, 0, 3, 0), (1, 0, 0, 0)] and slots == 3
     assert plan_ref.export([0, 600, 600, 610], 1, chunk_tokens=256) == (
-        [3, 4, 2, 3, 0, 1, 2, 4, 0, 0, 192, 0, 0, 192, 416, 1, 0, 416, 600, 2, 2, 0, 10, -1,
+        [3, 4, 2, 3, 0, 1, 2, 4, 0, 0, 224, 0, 0, 224, 448, 1, 0, 448, 600, 2, 2, 0, 10, -1,
          0, 0, 3, 0, 1, 0, 0, 0])
 
 
-def test_plan_snap_ties_and_sequence_end():
-    # a cut at 80 = 2.5 tiles into the sequence (a tie) goes down to 64
+def test_plan_small_hand_examples():
+    # 160 tokens, 2 workers: budget 128 gives 96 + (64 + 32); 127 gives 64 a worker
     pw, _, _ = plan_ref.make_plan([0, 160], 1, chunk_tokens=80)
-    assert [s[:3] for ws in pw for s in ws] == [(0, 0, 64), (0, 64, 160)]
-    # a cut at 115 (3.6 tiles into a 120-token sequence) stops at its end
+    assert [s[:3] for ws in pw for s in ws] == [(0, 0, 96), (0, 96, 160)]
+    # two sequences of 120 and 110 tokens, 2 workers: each whole (costs 160 and 144)
     pw, _, _ = plan_ref.make_plan([0, 120, 230], 1, chunk_tokens=115)
     assert pw == [[(0, 0, 120, -1)], [(1, 0, 110, -1)]]
-    # shares under SNAP_MIN_SHARE are not moved
+    # 96 tokens, 2 workers: budget 96 gives 64 + (32 + 32)
     pw, _, _ = plan_ref.make_plan([0, 96], 1, chunk_tokens=48)
-    assert [s[:3] for ws in pw for s in ws] == [(0, 0, 48), (0, 48, 96)]
+    assert [s[:3] for ws in pw for s in ws] == [(0, 0, 64), (0, 64, 96)]
+    # a short sequence shares a worker with the start of a long one: budget
+    # 128 holds sequence 0 (32 + 32) and one tile of sequence 1 (32 + 32)
+    pw, _, _ = plan_ref.make_plan([0, 20, 100], 1, chunk_tokens=50)
+    assert pw == [[(0, 0, 20, -1), (1, 0, 32, 0)], [(1, 32, 80, 1)]]

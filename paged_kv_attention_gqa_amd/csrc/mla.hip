@@ -28,12 +28,18 @@
 //   never rewritten transposed. The S^T accumulator already holds each lane's
 //   P^T operand (head = lane % 16, tokens 16h + 4c + j), as in the GQA kernel.
 // * A tile is 32 gathered rows (36 KB): sixteen threads per row load it with
-//   16-byte loads (consecutive lanes on consecutive bytes) into registers one
-//   two tiles ahead of the compute (list entries three tiles ahead), then
-//   store it to one of two LDS buffers whose rows are padded to 1184 bytes
-//   (the padding measured fastest among 1168-1280 bytes).
-// * A masked entry loads row 0 (so the data is finite) and gets score -inf.
-//   A piece with no valid entry gives out 0 and lse -inf.
+//   16-byte loads (consecutive lanes on consecutive bytes) into registers two
+//   tiles ahead of the compute, then store it to one of three LDS buffers
+//   whose rows are padded to 1184 bytes (the padding measured fastest among
+//   1168-1280 bytes). One barrier per tile: in the step that finishes tile t
+//   (softmax and P.V) each wave also computes its half scores of tile t+1,
+//   whose MFMAs overlap the softmax, and the workgroup stores tile t+2.
+// * The running max that the exponentials are taken against moves only when
+//   a head's max grows by more than 8 (log2 units), so the accumulators are
+//   rescaled on few tiles; p stays below 2^8, well inside fp32 and bf16.
+// * A masked entry is neither loaded nor stored: its score is -inf (weight 0)
+//   and its LDS row keeps older finite data (the buffers start zeroed). A
+//   piece with no valid entry gives out 0 and lse -inf.
 // * Optional per-row list lengths (HAVE_TOPK_LENGTH on the page) shorten each
 //   piece to the entries before min(max(len, 0), topk). An optional sink logit
 //   per head (HAVE_ATTN_SINK) joins the softmax denominator with no value:
@@ -65,6 +71,7 @@ constexpr int kQSteps = kMlaDqk / 32 / 2;          // 9 k-steps of 32 dims per h
 constexpr int kVBlocks = kMlaDv / 16 / 2;          // 16 blocks of 16 dims per half
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleSlack = 8.0f;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
@@ -94,23 +101,23 @@ struct StagedBf16 {
 
   __device__ __forceinline__ void load(int32_t id, int64_t pool_tokens, const void* kv) {
     valid = id >= 0 && static_cast<int64_t>(id) < pool_tokens;
-    const uint16_t* src = static_cast<const uint16_t*>(kv) +
-                          static_cast<int64_t>(valid ? id : 0) * kMlaDqk +
+    if (!valid) return;
+    const uint16_t* src = static_cast<const uint16_t*>(kv) + static_cast<int64_t>(id) * kMlaDqk +
                           (threadIdx.x % kThreadsPerRow) * 8;
 #pragma unroll
     for (int u = 0; u < kLoadsPerThread; ++u)
       if (has_unit(u)) v[u] = *reinterpret_cast<const u32x4*>(src + u * kThreadsPerRow * 8);
   }
 
-  // A masked row is stored as zeros, so its (zero-weight) V never meets a NaN.
+  // A masked row is not stored; only its flag is cleared.
   __device__ __forceinline__ void store(uint16_t* buf, uint8_t* vflag) const {
     const int row = threadIdx.x / kThreadsPerRow;
     uint16_t* dst = buf + row * kRowU16 + (threadIdx.x % kThreadsPerRow) * 8;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
+    if (threadIdx.x % kThreadsPerRow == 0) vflag[row] = valid ? 1 : 0;
+    if (!valid) return;
 #pragma unroll
     for (int u = 0; u < kLoadsPerThread; ++u)
-      if (has_unit(u)) *reinterpret_cast<u32x4*>(dst + u * kThreadsPerRow * 8) = valid ? v[u] : zero;
-    if (threadIdx.x % kThreadsPerRow == 0) vflag[row] = valid ? 1 : 0;
+      if (has_unit(u)) *reinterpret_cast<u32x4*>(dst + u * kThreadsPerRow * 8) = v[u];
   }
 };
 
@@ -128,9 +135,9 @@ struct StagedFp8 {
 
   __device__ __forceinline__ void load(int32_t id, int64_t pool_tokens, const void* kv) {
     valid = id >= 0 && static_cast<int64_t>(id) < pool_tokens;
+    if (!valid) return;
     const int j = threadIdx.x % kThreadsPerRow;
-    const uint8_t* src = static_cast<const uint8_t*>(kv) +
-                         static_cast<int64_t>(valid ? id : 0) * kMlaFp8TokenBytes;
+    const uint8_t* src = static_cast<const uint8_t*>(kv) + static_cast<int64_t>(id) * kMlaFp8TokenBytes;
     codes[0] = *reinterpret_cast<const u32x4*>(src + 16 * j);
     codes[1] = *reinterpret_cast<const u32x4*>(src + 256 + 16 * j);
     scales = *reinterpret_cast<const u32x4*>(src + 512);
@@ -141,6 +148,8 @@ struct StagedFp8 {
     const int row = threadIdx.x / kThreadsPerRow;
     const int j = threadIdx.x % kThreadsPerRow;
     uint16_t* dst = buf + row * kRowU16;
+    if (j == 0) vflag[row] = valid ? 1 : 0;
+    if (!valid) return;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       // values 256u + 16j .. +16 lie in the 128-value block 2u + j / 8 (the
@@ -157,18 +166,13 @@ struct StagedFp8 {
         packed[2 * wd] = bf16_pair(lo[0] * sc, lo[1] * sc);
         packed[2 * wd + 1] = bf16_pair(hi[0] * sc, hi[1] * sc);
       }
-      const u32x4 zero = {0u, 0u, 0u, 0u};
       const u32x4 a = {packed[0], packed[1], packed[2], packed[3]};
       const u32x4 b = {packed[4], packed[5], packed[6], packed[7]};
       uint16_t* d = dst + 256 * u + 16 * j;
-      *reinterpret_cast<u32x4*>(d) = valid ? a : zero;
-      *reinterpret_cast<u32x4*>(d + 8) = valid ? b : zero;
+      *reinterpret_cast<u32x4*>(d) = a;
+      *reinterpret_cast<u32x4*>(d + 8) = b;
     }
-    if (j < 8) {
-      const u32x4 zero = {0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(dst + 512 + 8 * j) = valid ? tail : zero;
-    }
-    if (j == 0) vflag[row] = valid ? 1 : 0;
+    if (j < 8) *reinterpret_cast<u32x4*>(dst + 512 + 8 * j) = tail;
   }
 };
 
@@ -224,21 +228,28 @@ __device__ __forceinline__ void softmax_pv(const uint16_t* buf, const uint8_t* v
   }
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
+  // The reference max moves only when a head's max grows by more than
+  // kRescaleSlack (log2 units), so the accumulators are rarely rescaled;
+  // meanwhile p stays below 2^kRescaleSlack.
   const float m_new = fmaxf(st.m, mx);
-  const float m_use = (m_new == kNegInf) ? 0.f : m_new;   // no valid entry yet
-  const float alpha = __builtin_amdgcn_exp2f(st.m - m_use);
+  const bool grow = m_new > st.m + kRescaleSlack;   // false while both are -inf
+  if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+    asm volatile("" ::: "memory");   // keeps this rarely taken block a branch
+    const float m_ref = grow ? m_new : st.m;
+    const float alpha = grow ? __builtin_amdgcn_exp2f(st.m - m_ref) : 1.0f;   // 0 from -inf
+    st.l *= alpha;
+#pragma unroll
+    for (int db = 0; db < kVBlocks; ++db) st.acc[db] *= alpha;
+    st.m = m_ref;
+  }
+  const float m_use = (st.m == kNegInf) ? 0.f : st.m;   // no valid entry yet: every p is 0
   float psum = 0.f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     p[j] = __builtin_amdgcn_exp2f(p[j] - m_use);
     psum += p[j];
   }
-  st.l = st.l * alpha + psum;
-  st.m = m_new;
-  if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {   // skip when no head's max moved
-#pragma unroll
-    for (int db = 0; db < kVBlocks; ++db) st.acc[db] *= alpha;
-  }
+  st.l += psum;
   bf16x8 pb;
 #pragma unroll
   for (int j = 0; j < 8; ++j) pb[j] = static_cast<__bf16>(p[j]);
@@ -270,9 +281,9 @@ __global__ __launch_bounds__(kThreads) void mla_partial_kernel(
     float scale_log2, const float* __restrict__ attn_sink, const int32_t* __restrict__ topk_length,
     uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
     float* __restrict__ part_lse) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kBufU16];
-  __shared__ uint8_t vflag[2][kTileTok];
-  __shared__ f32x4 xscore[8][2][64];   // each wave's half scores, [wave][mb][lane]
+  __shared__ __attribute__((aligned(16))) uint16_t lds[3 * kBufU16];
+  __shared__ uint8_t vflag[3][kTileTok];
+  __shared__ f32x4 xscore[2][8][2][64];   // half scores by tile parity, [wave][mb][lane]
   const int piece = blockIdx.x;
   const int hb = blockIdx.y;
   const int b = blockIdx.z;
@@ -306,36 +317,66 @@ __global__ __launch_bounds__(kThreads) void mla_partial_kernel(
   st.m = kNegInf;
   st.l = 0.f;
 
-  // Pipeline: row data two tiles ahead in two register sets, list entries
-  // three tiles ahead. Loads past the end are issued anyway (entry -1: row 0,
-  // masked) so that every load is unconditional.
+  // Pipeline over three LDS tile buffers with one barrier per tile: in step t
+  // the workgroup stores tile t+2 (loaded two steps earlier into one of two
+  // register sets) and reloads that set with tile t+4, finishes tile t
+  // (partner's half scores, softmax, P.V) and computes its half scores of
+  // tile t+1. Entries past the piece read as -1 (masked, nothing loaded).
   const int n_tiles = n > 0 ? (n + kTileTok - 1) / kTileTok : 0;
   Staged sa, sb;
-  sa.load(tile_entry(idx, 0, n), pool_tokens, kv);
-  sb.load(tile_entry(idx, kTileTok, n), pool_tokens, kv);
-  int32_t id_next = tile_entry(idx, 2 * kTileTok, n);
-  for (int t = 0; t < n_tiles; t += 2) {
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
+  if (n_tiles > 0) {
+    // A masked row is neither loaded nor stored, so its slot keeps older data:
+    // zeros from here, or a row staged for an earlier tile. Either is finite
+    // unless the pool itself holds a non-finite value in a row that was used.
+    {
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      for (int i = threadIdx.x; i < 3 * kBufU16 / 8; i += kThreads)
+        reinterpret_cast<u32x4*>(lds)[i] = zero;
+    }
+    sa.load(tile_entry(idx, 0, n), pool_tokens, kv);
+    sb.load(tile_entry(idx, kTileTok, n), pool_tokens, kv);
+    int32_t id_a = tile_entry(idx, 2 * kTileTok, n);
+    int32_t id_b = tile_entry(idx, 3 * kTileTok, n);
+    sa.store(lds, vflag[0]);
+    sa.load(id_a, pool_tokens, kv);                 // tile 2
+    sb.store(lds + kBufU16, vflag[1]);
+    sb.load(id_b, pool_tokens, kv);                 // tile 3
+    id_a = tile_entry(idx, 4 * kTileTok, n);
+    id_b = tile_entry(idx, 5 * kTileTok, n);
+    __syncthreads();
+    if (group_ok) {
+      half_scores(lds, qf, half, r, c, s0, s1);
+      xscore[0][w][0][lane] = s0;
+      xscore[0][w][1][lane] = s1;
+    }
+    __syncthreads();
+    int cur = 0;                                    // buffer of tile t
+    for (int t = 0; t < n_tiles; t += 2) {
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      if (k == 1 && t + 1 >= n_tiles) break;
-      Staged& cur = k == 0 ? sa : sb;
-      uint16_t* buf = lds + k * kBufU16;
-      const int32_t id_after = tile_entry(idx, (t + k + 3) * kTileTok, n);
-      cur.store(buf, vflag[k]);
-      cur.load(id_next, pool_tokens, kv);   // tile t + k + 2
-      id_next = id_after;
-      __syncthreads();   // tile t+k is in LDS; every wave is done with this buffer's last tile
-      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
-      if (group_ok) {
-        half_scores(buf, qf, half, r, c, s0, s1);
-        xscore[w][0][lane] = s0;
-        xscore[w][1][lane] = s1;
-      }
-      __syncthreads();   // both halves of every head group's scores are in LDS
-      if (group_ok) {
-        s0 += xscore[partner][0][lane];
-        s1 += xscore[partner][1][lane];
-        softmax_pv(buf, vflag[k], s0, s1, scale_log2, half, r, c, st);
+      for (int k = 0; k < 2; ++k) {
+        if (k == 1 && t + 1 >= n_tiles) break;
+        const int tt = t + k;
+        Staged& set = k == 0 ? sa : sb;
+        int32_t& id_set = k == 0 ? id_a : id_b;
+        const int nxt = cur == 2 ? 0 : cur + 1;     // buffer of tile tt+1
+        const int far = nxt == 2 ? 0 : nxt + 1;     // buffer of tile tt+2
+        set.store(lds + far * kBufU16, vflag[far]); // tile tt+2
+        set.load(id_set, pool_tokens, kv);          // tile tt+4
+        id_set = tile_entry(idx, (tt + 6) * kTileTok, n);
+        if (group_ok) {
+          const f32x4 f0 = s0 + xscore[tt & 1][partner][0][lane];
+          const f32x4 f1 = s1 + xscore[tt & 1][partner][1][lane];
+          // Scores of tile tt+1 first (in the last step they are computed from
+          // a buffer holding finite older data and never used): their MFMAs
+          // run while the softmax of tile tt is on the vector ALU.
+          half_scores(lds + nxt * kBufU16, qf, half, r, c, s0, s1);
+          softmax_pv(lds + cur * kBufU16, vflag[cur], f0, f1, scale_log2, half, r, c, st);
+          xscore[(tt + 1) & 1][w][0][lane] = s0;
+          xscore[(tt + 1) & 1][w][1][lane] = s1;
+        }
+        __syncthreads();
+        cur = nxt;
       }
     }
   }

@@ -49,6 +49,7 @@ WORKLOAD_TEXT = {
 }
 KERNEL_SRC = os.path.join(ROOT, "paged_kv_attention_gqa_amd", "csrc", "decode.hip")
 PLAN_SRC = os.path.join(ROOT, "paged_kv_attention_gqa_amd", "csrc", "plan.cpp")
+MLA_SRC = os.path.join(ROOT, "paged_kv_attention_gqa_amd", "csrc", "mla.hip")
 
 
 def traffic_file(config: str) -> str:
@@ -77,21 +78,20 @@ def algorithmic_decode_bytes(w, plan_flat) -> int:
             + n_slots * (16384 + 128) + 32 * max(n_segs, n_workers))
 
 
-def sources_sha256() -> str:
-    """sha256 over the decode kernel's source and the partition rule's source,
-    the two files the counted bytes of one launch depend on."""
+def sources_sha256(paths=(KERNEL_SRC, PLAN_SRC)) -> str:
+    """sha256 over the sources the counted bytes of one launch depend on (for
+    the decode kernel: its source and the partition rule's source)."""
     import hashlib
     h = hashlib.sha256()
-    for path in (KERNEL_SRC, PLAN_SRC):
+    for path in paths:
         h.update(open(path, "rb").read())
     return h.hexdigest()
 
 
-def read_traffic(config: str):
+def read_traffic(config: str, path: str = None, sources=(KERNEL_SRC, PLAN_SRC)):
     """HBM bytes per launch from the committed counter summary of this workload,
-    or None if there is none or the kernel or the partition rule has changed
-    since."""
-    path = traffic_file(config)
+    or None if there is none or the sources it was taken with have changed."""
+    path = path or traffic_file(config)
     if not os.path.exists(path):
         return None
     vals = {}
@@ -99,12 +99,23 @@ def read_traffic(config: str):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("sources_sha256") != sources_sha256():
+    if vals.get("sources_sha256") != sources_sha256(sources):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def calibration_copy():
+    """A plain 1 GiB device copy, three times: the reference dispatch that the
+    FETCH_SIZE / WRITE_SIZE counter runs are scaled by."""
+    import torch
+    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
 
 
 def cpu_baseline(w, budget_s: float):
@@ -176,6 +187,8 @@ def bench_mla(args):
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / args.steps
+    if args.calib_copy:
+        calibration_copy()
     call_s = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
     valid = int((w.indices >= 0).sum())
     flops = 2.0 * w.num_qo_heads * valid * (w.d_qk + w.d_v)
@@ -193,7 +206,10 @@ def bench_mla(args):
                    "pool_replicas": reps},
         "roofline": {"bound": "mfma", "achieved": round(flops / call_s / 1e12, 2), "peak": 2500.0,
                      "unit": "TFLOP/s", "frac": round(flops / call_s / 1e12 / 2500.0, 4),
-                     "traffic": None, "kernel": "mla_partial_kernel + mla_merge_kernel",
+                     "traffic": read_traffic(args.config, os.path.join(
+                         ROOT, "profiles", f"mla_partial_{args.config}_traffic.txt"), (MLA_SRC,)),
+                     "traffic_kernel": "mla_partial_kernel",
+                     "kernel": "mla_partial_kernel + mla_merge_kernel",
                      "call_avg_us": round(call_s * 1e6, 3),
                      "algorithmic_flops_per_call": flops, "gathered_bytes_per_call": gathered,
                      "hbm_frac_of_gathered": round(gathered / call_s / 1e9 / PEAK_HBM_GBS, 4)},
@@ -395,11 +411,7 @@ def main():
     wall = time.perf_counter() - t0
 
     if args.calib_copy:
-        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
+        calibration_copy()
 
     decode_ms = np.array([a.elapsed_time(b) for a, b in ev.values()])
     decode_s = float(decode_ms.mean()) / 1e3

@@ -11,6 +11,10 @@
 // Design:
 // * Work is split three ways: row b, a block of up to 64 query heads, and a
 //   contiguous piece of the index list; one workgroup of 8 waves per triple.
+//   The two head blocks of one (row, piece) are launched 8 workgroups apart,
+//   so they run on the same XCD and the second gather of a tile mostly hits
+//   in that XCD's L2 (without this the memory-side fetches were twice the
+//   gathered bytes).
 //   Wave w owns 16 heads (w % 4) and one half (w / 4) of both contractions:
 //   dims [288 half, +288) of the 576-dim scores and dims [256 half, +256) of
 //   the 512-dim output. The two waves of a head group swap their partial
@@ -277,17 +281,23 @@ __device__ __forceinline__ void softmax_pv(const uint16_t* buf, const uint8_t* v
 template <typename Staged>
 __global__ __launch_bounds__(kThreads) void mla_partial_kernel(
     const uint16_t* __restrict__ q, const void* __restrict__ kv, int64_t pool_tokens,
-    const int32_t* __restrict__ indices, int topk, int num_qo_heads, int per_piece,
-    float scale_log2, const float* __restrict__ attn_sink, const int32_t* __restrict__ topk_length,
-    uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
-    float* __restrict__ part_lse) {
+    const int32_t* __restrict__ indices, int topk, int num_qo_heads, int per_piece, int pieces,
+    int hblocks, int batch, float scale_log2, const float* __restrict__ attn_sink,
+    const int32_t* __restrict__ topk_length, uint16_t* __restrict__ out, float* __restrict__ lse,
+    float* __restrict__ part_o, float* __restrict__ part_lse) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[3 * kBufU16];
   __shared__ uint8_t vflag[3][kTileTok];
   __shared__ f32x4 xscore[2][8][2][64];   // half scores by tile parity, [wave][mb][lane]
-  const int piece = blockIdx.x;
-  const int hb = blockIdx.y;
-  const int b = blockIdx.z;
-  const int pieces = gridDim.x;
+  // Workgroups are dealt to the XCDs in turn (workgroup i to XCD i % 8). With
+  // two head blocks, workgroups 16 g + x and 16 g + 8 + x (x < 8) are the two
+  // head blocks of one (row, piece), so they share an XCD and its L2, and the
+  // second gather of each tile mostly hits there.
+  const int wg = blockIdx.x;
+  const int pair = hblocks == 2 ? (wg >> 4) * 8 + (wg & 7) : wg;
+  const int hb = hblocks == 2 ? (wg >> 3) & 1 : 0;
+  if (pair >= pieces * batch) return;   // padding of the last group of 16
+  const int b = pair / pieces;
+  const int piece = pair - b * pieces;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int hg = w & 3;          // head group
@@ -484,14 +494,18 @@ hipError_t launch_gather_mla(const uint16_t* q, const void* kv_pool, bool fp8_po
   float* part_o = static_cast<float*>(workspace);
   float* part_lse = pieces > 1 ? part_o + static_cast<size_t>(batch) * num_qo_heads * pieces * kMlaDv : nullptr;
   const float scale_log2 = sm_scale * 1.4426950408889634f;
+  const int pairs = pieces * batch;
+  const int grid = hblocks == 2 ? 16 * ((pairs + 7) / 8) : pairs;
   if (fp8_pool) {
-    hipLaunchKernelGGL(mla_partial_kernel<StagedFp8>, dim3(pieces, hblocks, batch), dim3(kThreads),
-                       0, stream, q, kv_pool, pool_tokens, indices, topk, num_qo_heads, per_piece,
-                       scale_log2, attn_sink, topk_length, out, lse, part_o, part_lse);
+    hipLaunchKernelGGL(mla_partial_kernel<StagedFp8>, dim3(grid), dim3(kThreads), 0, stream, q,
+                       kv_pool, pool_tokens, indices, topk, num_qo_heads, per_piece, pieces,
+                       hblocks, batch, scale_log2, attn_sink, topk_length, out, lse, part_o,
+                       part_lse);
   } else {
-    hipLaunchKernelGGL(mla_partial_kernel<StagedBf16>, dim3(pieces, hblocks, batch), dim3(kThreads),
-                       0, stream, q, kv_pool, pool_tokens, indices, topk, num_qo_heads, per_piece,
-                       scale_log2, attn_sink, topk_length, out, lse, part_o, part_lse);
+    hipLaunchKernelGGL(mla_partial_kernel<StagedBf16>, dim3(grid), dim3(kThreads), 0, stream, q,
+                       kv_pool, pool_tokens, indices, topk, num_qo_heads, per_piece, pieces,
+                       hblocks, batch, scale_log2, attn_sink, topk_length, out, lse, part_o,
+                       part_lse);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pieces == 1) return e;

@@ -59,6 +59,22 @@ def test_mla_masking_rules():
     assert np.max(np.abs(got[0][3] - single)) <= 1e-2
 
 
+def test_mla_unlisted_rows_are_never_read():
+    """Every pool row that no valid entry lists holds NaN. Masked entries (-1,
+    past the pool end, a masked tail spanning whole pieces) read nothing, so
+    the output stays finite and equal to the oracle's."""
+    w = make_mla(53, batch=3, num_qo_heads=128, pool_tokens=2000, topk=300, masked_per_row=40)
+    idx = w.indices.copy()
+    idx[1, ::5] = w.pool_tokens + 1
+    idx[2, 100:] = -1
+    listed = np.unique(idx[(idx >= 0) & (idx < w.pool_tokens)])
+    unlisted = np.setdiff1d(np.arange(w.pool_tokens), listed)
+    w.kv_pool[unlisted] = 0x7FC0                    # bf16 quiet NaN
+    got = run_gpu(w, idx)
+    assert np.all(np.isfinite(got[0]))
+    check(w, got, idx, "unlisted rows NaN")
+
+
 def test_mla_scale_and_rerun():
     w = make_mla(52, batch=2, num_qo_heads=128, pool_tokens=3000, topk=512, sm_scale=0.11)
     a = run_gpu(w)

@@ -64,7 +64,8 @@ def test_fp8_shapes(heads, topk):
 
 
 def test_fp8_masking_with_nan_row_zero():
-    """Masked entries read pool row 0; NaN codes there must not reach the output."""
+    """Masked entries read no pool row; NaN codes in row 0, which no entry
+    lists, must not reach the output."""
     w = make_mla_fp8(65, batch=4, num_qo_heads=64, pool_tokens=900, topk=200, masked_per_row=20)
     w.kv_pool[0, :512] = 0x7F                                  # e4m3 NaN
     idx = w.indices.copy()
@@ -75,6 +76,23 @@ def test_fp8_masking_with_nan_row_zero():
     got = run_fp8(w, idx)
     check(w, got, "fp8 masking", indices=idx)
     assert np.all(got[0][0] == 0.0) and np.all(np.isneginf(got[1][0]))
+
+
+def test_fp8_unlisted_rows_are_never_read():
+    """Every token that no valid entry lists has NaN codes, NaN scales and a
+    NaN bf16 tail; the output stays finite and equal to the oracle's."""
+    w = make_mla_fp8(66, batch=3, num_qo_heads=64, pool_tokens=1500, topk=300, masked_per_row=40)
+    idx = w.indices.copy()
+    idx[1, ::5] = w.pool_tokens + 1
+    idx[2, 100:] = -1
+    listed = np.unique(idx[(idx >= 0) & (idx < w.pool_tokens)])
+    unlisted = np.setdiff1d(np.arange(w.pool_tokens), listed)
+    w.kv_pool[unlisted, :512] = 0x7F                              # e4m3 NaN
+    w.kv_pool[unlisted, 512:528] = np.frombuffer(np.full(4, np.nan, np.float32).tobytes(), np.uint8)
+    w.kv_pool[unlisted, 528:] = np.frombuffer(np.full(64, 0x7FC0, np.uint16).tobytes(), np.uint8)
+    got = run_fp8(w, idx)
+    assert np.all(np.isfinite(got[0]))
+    check(w, got, "fp8 unlisted rows NaN", indices=idx)
 
 
 def test_fp8_sink_and_lengths():

@@ -139,6 +139,10 @@ def cpu_baseline(w, budget_s: float):
     per_call = t_total / reps
     return {"value": 2048.0 * w.total_tokens / per_call / 1e9, "unit": "GB/s", "cores": cores,
             "kind": "oracle", "us_per_call": per_call * 1e6,
+            "decode_tokens_per_s": w.batch / per_call,
+            "kv_tokens_per_s": w.total_tokens / per_call,
+            "affinity_cores": len(os.sched_getaffinity(0)),
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
             "sample": f"whole batch ({w.batch} sequences, {w.total_tokens} tokens), {reps} runs, "
                       f"{t_total:.1f} s"}
 
@@ -449,6 +453,7 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "kernel": "decode_partial_kernel",
                      "kernel_avg_us": round(decode_s * 1e6, 3),
+                     "kernel_median_us": round(float(np.median(decode_ms)) * 1e3, 3),
                      "kernel_p10_us": round(float(np.percentile(decode_ms, 10)) * 1e3, 3),
                      "kernel_p90_us": round(float(np.percentile(decode_ms, 90)) * 1e3, 3),
                      "kernel_samples": len(decode_ms),

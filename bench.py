@@ -50,6 +50,7 @@ WORKLOAD_TEXT = {
 KERNEL_SRC = os.path.join(ROOT, "paged_kv_attention_gqa_amd", "csrc", "decode.hip")
 PLAN_SRC = os.path.join(ROOT, "paged_kv_attention_gqa_amd", "csrc", "plan.cpp")
 MLA_SRC = os.path.join(ROOT, "paged_kv_attention_gqa_amd", "csrc", "mla.hip")
+APPEND_SRC = os.path.join(ROOT, "paged_kv_attention_gqa_amd", "csrc", "append.hip")
 
 
 def traffic_file(config: str) -> str:
@@ -277,6 +278,8 @@ def bench_append(args):
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / args.steps
+    if args.calib_copy:
+        calibration_copy()
     call_s = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
     alg = 4096 * valid + 8 * n
     rec = {
@@ -289,7 +292,9 @@ def bench_append(args):
                    "row_replicas": reps},
         "roofline": {"bound": "hbm", "achieved": round(alg / call_s / 1e9, 2),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(alg / call_s / 1e9 / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(alg / call_s / 1e9 / PEAK_HBM_GBS, 4),
+                     "traffic": read_traffic("append", os.path.join(
+                         ROOT, "profiles", "append_kernel_append_traffic.txt"), (APPEND_SRC,)),
                      "kernel": "append_kernel", "call_avg_us": round(call_s * 1e6, 3),
                      "algorithmic_bytes_per_launch": alg},
     }

@@ -29,8 +29,9 @@
 // * K/V rows are gathered straight into registers: lane (r, c) reads bytes
 //   [64x + 16c, +16) of the 256-byte (page, KV head) row of token 16*mb + r,
 //   so one load instruction covers 64 contiguous bytes of 16 rows.
-// * V is written to LDS row-major (272-byte padded rows, conflict-free) and
-//   read back transposed (8 tokens of one dim per lane) as the A operand.
+// * V is written to LDS row-major (288-byte padded rows) and read back as the
+//   transposed A operand (8 tokens of one dim per lane) with the
+//   transposing LDS load ds_read_b64_tr_b16, two per 16-dim block.
 // * Loads are software-pipelined one tile ahead (page ids two tiles ahead);
 //   out-of-range tokens of the last tile re-read the item's last page, which
 //   keeps every load unconditional, and get score -inf, i.e. weight exactly 0.
@@ -48,11 +49,11 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kGroup = kHq / kHkv;      // query heads per KV head
 constexpr int kTileTok = 32;            // tokens per wave per step
-constexpr int kRowU16 = kHeadDim + 8;   // LDS row of one token's V: 256 B + 16 B pad
+constexpr int kRowU16 = kHeadDim + 16;  // LDS row of one token's V: 256 B + 32 B pad
 constexpr int kWaveLdsU16 = kTileTok * kRowU16;
 constexpr int kThreads = 64 * kHkv;
 constexpr int kPipeTiles = 2;           // register tile buffers per wave
@@ -150,16 +151,21 @@ __device__ __forceinline__ void compute_tile(const Tile& t, int t0, int n, const
 #pragma unroll
   for (int j = 0; j < 8; ++j) pb[j] = static_cast<__bf16>(p[j]);
 
-  // A operand of block db: V[token 16*(j/4) + 4c + j%4][16*db + r], j = 0..7.
+  // A operand of block db: V[token 16*(j/4) + 4c + j%4][16*db + r], j = 0..7,
+  // read with the transposing LDS load: within each 16-lane group it gives
+  // lane i element i%4 of the 8-byte chunks addressed by lanes 4j + i/4, so
+  // lane (r, c) points at token 4c + r/4 (and 16 more), dims 16 db + 4 (r%4).
+  const uint16_t* vrow0 = lw + (4 * c + (r >> 2)) * kRowU16 + 4 * (r & 3);
+  const uint16_t* vrow1 = vrow0 + 16 * kRowU16;
 #pragma unroll
   for (int db = 0; db < 8; ++db) {
-    u16x8 e;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      e[j] = lw[(16 * (j >> 2) + 4 * c + (j & 3)) * kRowU16 + 16 * db + r];
-    }
-    st.acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, e), pb,
-                                                         st.acc[db], 0, 0, 0);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(vrow0 + 16 * db));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(vrow1 + 16 * db));
+    const u32x4 a = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                     __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
+    st.acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), pb, st.acc[db], 0, 0, 0);
   }
 }
 

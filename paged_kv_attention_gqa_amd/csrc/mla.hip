@@ -346,6 +346,7 @@ __global__ __launch_bounds__(kThreads) void mla_partial_kernel(
     }
     sa.load(tile_entry(idx, 0, n), pool_tokens, kv);
     sb.load(tile_entry(idx, kTileTok, n), pool_tokens, kv);
+    __syncthreads();   // every wave's zeros land before any wave stores a row
     int32_t id_a = tile_entry(idx, 2 * kTileTok, n);
     int32_t id_b = tile_entry(idx, 3 * kTileTok, n);
     sa.store(lds, vflag[0]);

@@ -179,7 +179,9 @@ struct TokenRows<false> {
   const int32_t* ids;   // page ids of the segment's tokens
   __device__ TokenRows(const KvAddressing& a, int b, int lo, int seq_offset)
       : ids(a.ids + seq_offset + lo) {}
-  __device__ __forceinline__ int32_t operator()(int j) const { return ids[j]; }
+  __device__ __forceinline__ int32_t fetch(int j) const { return ids[j]; }
+  __device__ __forceinline__ int32_t row_of(int32_t fetched, int) const { return fetched; }
+  __device__ __forceinline__ int32_t operator()(int j) const { return row_of(fetch(j), j); }
 };
 
 // Block table: token t = lo + j of sequence b is slot t % ps of page row[t / ps].
@@ -190,10 +192,11 @@ struct TokenRows<true> {
   __device__ TokenRows(const KvAddressing& a, int b, int lo_, int)
       : row(a.ids + static_cast<int64_t>(b) * a.table_stride), lo(lo_), shift(a.page_shift),
         mask((1 << a.page_shift) - 1) {}
-  __device__ __forceinline__ int32_t operator()(int j) const {
-    const int t = lo + j;
-    return (row[t >> shift] << shift) | (t & mask);
+  __device__ __forceinline__ int32_t fetch(int j) const { return row[(lo + j) >> shift]; }
+  __device__ __forceinline__ int32_t row_of(int32_t page, int j) const {
+    return (page << shift) | ((lo + j) & mask);
   }
+  __device__ __forceinline__ int32_t operator()(int j) const { return row_of(fetch(j), j); }
 };
 
 // Decodes tokens [lo, lo + n) of sequence b (n > 0) with all four waves of the
@@ -243,15 +246,19 @@ __device__ __forceinline__ void process_segment(
   // buffers the final iterations loaded.
   const int n_tiles = (n + kTileTok - 1) / kTileTok;
   const int n_rounds = n_tiles / kPipeTiles;
+  static_assert(kPipeTiles == 2, "the prologue below fills a ring of two tiles");
   Tile ring[kPipeTiles];
-#pragma unroll
-  for (int k = 0; k < kPipeTiles - 1; ++k) {
-    const int32_t a0 = ids(min(kTileTok * k + r, last));
-    const int32_t a1 = ids(min(kTileTok * k + 16 + r, last));
-    load_tile(ring[k], k_pool, v_pool, a0, a1, g, c);
-  }
-  int32_t next0 = ids(min(kTileTok * (kPipeTiles - 1) + r, last));
-  int32_t next1 = ids(min(kTileTok * (kPipeTiles - 1) + 16 + r, last));
+  // The ids of the first two tiles are fetched together, before any K/V load,
+  // so the loop starts with the second tile's rows known and no load pending
+  // but the first tile's.
+  const int ja0 = min(r, last), ja1 = min(16 + r, last);
+  const int jn0 = min(kTileTok + r, last), jn1 = min(kTileTok + 16 + r, last);
+  int32_t a0 = ids.fetch(ja0), a1 = ids.fetch(ja1);
+  int32_t n0 = ids.fetch(jn0), n1 = ids.fetch(jn1);
+  asm volatile("" : "+v"(a0), "+v"(a1), "+v"(n0), "+v"(n1));
+  load_tile(ring[0], k_pool, v_pool, ids.row_of(a0, ja0), ids.row_of(a1, ja1), g, c);
+  int32_t next0 = ids.row_of(n0, jn0);
+  int32_t next1 = ids.row_of(n1, jn1);
   int t0 = 0;
   for (int round = 0; round < n_rounds; ++round) {
 #pragma unroll
@@ -261,15 +268,21 @@ __device__ __forceinline__ void process_segment(
       // the tile after that.
       asm volatile("" ::: "memory");
       const int tf = t0 + kTileTok * (k + kPipeTiles);
-      const int32_t f0 = ids(min(tf + r, last));
-      const int32_t f1 = ids(min(tf + 16 + r, last));
+      const int j0 = min(tf + r, last);
+      const int j1 = min(tf + 16 + r, last);
+      int32_t f0 = ids.fetch(j0);
+      int32_t f1 = ids.fetch(j1);
       load_tile(ring[(k + kPipeTiles - 1) % kPipeTiles], k_pool, v_pool, next0, next1, g, c);
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
       compute_tile(ring[k], t0 + kTileTok * k, n, qf, scale_log2, r, c, lw, st);
       __builtin_amdgcn_sched_barrier(0);
-      next0 = f0;
-      next1 = f1;
+      // The fetched ids stay opaque until the compute above has been issued,
+      // so nothing derived from them is scheduled next to their loads (which
+      // would make the wave wait for loads it has just issued).
+      asm volatile("" : "+v"(f0), "+v"(f1));
+      next0 = ids.row_of(f0, j0);
+      next1 = ids.row_of(f1, j1);
     }
     t0 += kTileTok * kPipeTiles;
   }

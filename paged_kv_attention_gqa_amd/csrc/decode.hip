@@ -339,67 +339,102 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
 }
 
-// One workgroup per (split sequence, query head). The 256 threads form 8
-// groups of 32; group j takes chunks j, j+8, j+16, ... and each lane of a group
-// owns 4 consecutive dims. The groups' partial sums are combined in LDS in a
-// fixed order, so the result does not depend on timing.
-constexpr int kMergeGroups = 8;
+// One wave per (merge record, query head), four heads per workgroup. Lane
+// (p, e) = (lane / 16, lane % 16) owns dims [8e, 8e + 8) of the partials
+// i = 4j + p. The partials are taken in rounds of 4J: every load of a round
+// (one LSE per lane, two 16-byte loads per lane and partial) is issued before
+// any is used, and the round is folded into the running result against a
+// running maximum, so a sequence cut into up to ~120 pieces costs one round
+// trip to memory. The four lane groups are summed at the end in a fixed
+// order, so the result does not depend on timing.
+template <int J>
+__device__ __forceinline__ void merge_round(const float* part_o, const float* part_lse, int first,
+                                            int k,
+                                            int i0, int h, int lane, float& top, float& den,
+                                            f32x4 (&acc)[2]) {
+  const int p = lane >> 4;
+  const int e = lane & 15;
+  // LSE of partial i0 + lane (-inf past the end).
+  const int il = i0 + lane;
+  float li = part_lse[static_cast<int64_t>(first + min(il, k - 1)) * kHq + h];
+  f32x4 o[J][2];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int i = min(i0 + 4 * j + p, k - 1);
+    const float* src = part_o + (static_cast<int64_t>(first + i) * kHq + h) * kHeadDim + 8 * e;
+    o[j][0] = *reinterpret_cast<const f32x4*>(src);
+    o[j][1] = *reinterpret_cast<const f32x4*>(src + 4);
+  }
+  // Every load of the round is issued before the first of these statements
+  // (they clobber memory), and every use comes after its value passes one.
+  asm volatile("" : "+v"(li) :: "memory");
+#pragma unroll
+  for (int j = 0; j < J; ++j) asm volatile("" : "+v"(o[j][0]), "+v"(o[j][1]) :: "memory");
+  if (il >= k || lane >= 4 * J) li = kNegInf;
+  float mx = li;
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) mx = fmaxf(mx, __shfl_xor(mx, sh));
+  const float nt = fmaxf(top, mx);   // finite once any piece has a token
+  const float sc = nt == kNegInf ? 0.f : __builtin_amdgcn_exp2f(top - nt);
+  const float w = li == kNegInf ? 0.f : __builtin_amdgcn_exp2f(li - nt);
+  float ws = w;
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) ws += __shfl_xor(ws, sh);
+  den = den * sc + ws;
+  acc[0] *= sc;
+  acc[1] *= sc;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const float wi = __shfl(w, 4 * j + p);
+    acc[0] += wi * o[j][0];
+    acc[1] += wi * o[j][1];
+  }
+  top = nt;
+}
 
+// part_o and part_lse are not marked __restrict__: loads from restrict
+// read-only arguments may be re-issued next to their uses to save registers,
+// which would serialise the round's loads.
 __global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ merges,
-                                                    const float* __restrict__ part_o,
-                                                    const float* __restrict__ part_lse,
+                                                    const float* part_o, const float* part_lse,
                                                     uint16_t* __restrict__ out,
                                                     float* __restrict__ lse) {
-  __shared__ float s_top[kMergeGroups];
-  __shared__ float s_den[kMergeGroups];
-  __shared__ f32x4 s_acc[kMergeGroups][32];
   const int32_t* m = merges + 4 * blockIdx.x;
   const int b = m[0];
   const int first = m[1];
   const int k = m[2];
-  const int h = blockIdx.y;
-  const int grp = threadIdx.x >> 5;
-  const int d0 = (threadIdx.x & 31) * 4;
-
-  float top = kNegInf;
-  for (int i = grp; i < k; i += kMergeGroups)
-    top = fmaxf(top, part_lse[static_cast<int64_t>(first + i) * kHq + h]);
-  if ((threadIdx.x & 31) == 0) s_top[grp] = top;
-  __syncthreads();
-  top = s_top[0];
+  const int lane = threadIdx.x & 63;
+  const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
+  float top = kNegInf, den = 0.f;
+  f32x4 acc[2] = {};
+  if (k <= 16) {
+    if (k > 0) merge_round<4>(part_o, part_lse, first, k, 0, h, lane, top, den, acc);
+  } else {
+    for (int i0 = 0; i0 < k; i0 += 64)
+      merge_round<16>(part_o, part_lse, first, k, i0, h, lane, top, den, acc);
+  }
+  // Sum the four lane groups (lanes e, e + 16, e + 32, e + 48).
 #pragma unroll
-  for (int j = 1; j < kMergeGroups; ++j) top = fmaxf(top, s_top[j]);
-
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float den = 0.f;
-  if (top != kNegInf) {
-#pragma unroll 4
-    for (int i = grp; i < k; i += kMergeGroups) {
-      const int64_t slot = static_cast<int64_t>(first + i) * kHq + h;
-      const float li = part_lse[slot];
-      const float w = (li == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(li - top);
-      den += w;
-      acc += w * *reinterpret_cast<const f32x4*>(part_o + slot * kHeadDim + d0);
+  for (int x = 0; x < 2; ++x) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = acc[x][i];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      acc[x][i] = v;
     }
   }
-  s_acc[grp][threadIdx.x & 31] = acc;
-  if ((threadIdx.x & 31) == 0) s_den[grp] = den;
-  __syncthreads();
-  if (grp != 0) return;
-  acc = s_acc[0][threadIdx.x];
-  den = s_den[0];
-#pragma unroll
-  for (int j = 1; j < kMergeGroups; ++j) {
-    acc += s_acc[j][threadIdx.x];
-    den += s_den[j];
+  if (lane < 16) {
+    const float inv = den > 0.f ? 1.0f / den : 0.f;
+    const f32x4 a = acc[0] * inv;
+    const f32x4 c = acc[1] * inv;
+    const u32x4 w = {static_cast<uint32_t>(bf16_bits(a[0])) | (static_cast<uint32_t>(bf16_bits(a[1])) << 16),
+                     static_cast<uint32_t>(bf16_bits(a[2])) | (static_cast<uint32_t>(bf16_bits(a[3])) << 16),
+                     static_cast<uint32_t>(bf16_bits(c[0])) | (static_cast<uint32_t>(bf16_bits(c[1])) << 16),
+                     static_cast<uint32_t>(bf16_bits(c[2])) | (static_cast<uint32_t>(bf16_bits(c[3])) << 16)};
+    *reinterpret_cast<u32x4*>(out + (static_cast<int64_t>(b) * kHq + h) * kHeadDim + 8 * lane) = w;
+    if (lane == 0) lse[b * kHq + h] = den > 0.f ? top + __log2f(den) : kNegInf;
   }
-  const float inv = (den > 0.f) ? 1.0f / den : 0.f;
-  const u32x2 w = {static_cast<uint32_t>(bf16_bits(acc[0] * inv)) |
-                       (static_cast<uint32_t>(bf16_bits(acc[1] * inv)) << 16),
-                   static_cast<uint32_t>(bf16_bits(acc[2] * inv)) |
-                       (static_cast<uint32_t>(bf16_bits(acc[3] * inv)) << 16)};
-  *reinterpret_cast<u32x2*>(out + (static_cast<int64_t>(b) * kHq + h) * kHeadDim + d0) = w;
-  if (threadIdx.x == 0) lse[b * kHq + h] = (den > 0.f) ? top + __log2f(den) : kNegInf;
 }
 
 }  // namespace
@@ -425,9 +460,8 @@ hipError_t launch_decode_partial(const int32_t* workers, const int32_t* segments
 hipError_t launch_merge(const int32_t* merges, int32_t n_merges, const float* part_o,
                         const float* part_lse, uint16_t* out, float* lse, hipStream_t stream) {
   if (n_merges <= 0) return hipSuccess;
-  hipLaunchKernelGGL(merge_kernel, dim3(n_merges, kHq), dim3(256), 0, stream, merges, part_o,
-                     part_lse,
-                     out, lse);
+  hipLaunchKernelGGL(merge_kernel, dim3(n_merges, kHq / 4), dim3(256), 0, stream, merges, part_o,
+                     part_lse, out, lse);
   return hipGetLastError();
 }
 

@@ -32,7 +32,9 @@
  * pointers 16-byte aligned):
  *   q        bf16  [B, Hq, D]
  *   k_pool   bf16  [num_pages, page_size, Hkv, D]   (v_pool the same)
- *   kv_indptr int32 [B + 1]   (device copy; the plan reads a host copy)
+ *   kv_indptr int32 [B + 1]   (device copy: checked for non-NULL and length
+ *            only, never read by the kernels, which take every sequence's
+ *            token offset from the plan built from the host copy)
  *   kv_indices int32 [kv_indptr[B]], each in [0, num_pages)  (caller
  *            precondition, as in the page's kernel: not checked on device)
  *   out      bf16  [B, Hq, D]
@@ -96,6 +98,27 @@ pkv_status pkv_plan_create(const int32_t* kv_indptr_host, int32_t batch,
 void pkv_plan_destroy(pkv_plan* plan);
 
 /*
+ * Bytes of device workspace this plan needs (the same number
+ * pkv_workspace_size / pkv_block_table_workspace_size return for its batch),
+ * so that a caller can make a host-only plan, size and allocate the
+ * workspace, then bind it with pkv_plan_upload without building the
+ * partition twice. PKV_ERR_INVALID_ARG for a NULL argument.
+ */
+pkv_status pkv_plan_workspace_size(const pkv_plan* plan, size_t* bytes);
+
+/*
+ * Enqueue the upload of the plan's work tables into `workspace` on `stream`
+ * and bind the plan to it, exactly as passing the workspace to
+ * pkv_plan_create would have (a plan may be re-bound to another workspace;
+ * later runs must pass the workspace of the latest upload). The workspace must
+ * hold pkv_plan_workspace_size bytes (PKV_ERR_WORKSPACE_TOO_SMALL otherwise)
+ * and be 16-byte aligned (PKV_ERR_INVALID_ARG); PKV_ERR_HIP if the copy
+ * cannot be enqueued. The host tables stay owned by the plan, so it must
+ * outlive the copy (it does when it is destroyed after the stream's work).
+ */
+pkv_status pkv_plan_upload(pkv_plan* plan, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Copy the plan's integer tables to host memory:
  * [n_workers, n_segments, n_merges, n_slots], then n_workers + 1 offsets of
  * each worker's first segment, then n_segments records
@@ -118,8 +141,10 @@ pkv_status pkv_plan_export(const pkv_plan* plan, int32_t* dst, size_t n_int32, s
  * checked against the plan: q is [q_batch, q_heads, q_dim], each pool is
  * [num_pages, page_size, pool_kv_heads, pool_dim], kv_indptr has indptr_len
  * entries and kv_indices has num_indices entries (must equal the plan's
- * kv_indptr[B]). sm_scale must be finite (the Python layer fills the default
- * 1/sqrt(head_dim)).
+ * kv_indptr[B]). sm_scale may be any finite value (the Python layer fills the
+ * default 1/sqrt(head_dim)): the definition above holds for every real scale,
+ * 0 giving equal weights (the mean of the V rows) and a negative scale
+ * reversing the order of the scores; NaN or +-inf returns PKV_ERR_INVALID_ARG.
  */
 pkv_status pkv_run(const pkv_plan* plan,
                    const void* q, int32_t q_batch, int32_t q_heads, int32_t q_dim,
@@ -192,9 +217,11 @@ pkv_status pkv_merge(const pkv_plan* plan, void* workspace, size_t workspace_byt
  * slot % page_size of k_pool / v_pool (bf16 [num_pages, page_size,
  * num_kv_heads, head_dim]) with slot = slot_mapping[i] (device int64
  * [n_rows]); a slot outside [0, num_pages * page_size), e.g. -1 for padding,
- * stores nothing. The rows are copied bit for bit. Valid slots must be
- * distinct: two rows with the same slot race and the slot ends up holding
- * one of them. Any head count and head_dim whose row is a multiple of 16
+ * stores nothing. The rows are copied bit for bit. Valid slots should be
+ * distinct: rows that name the same slot race with nothing ordering their
+ * stores, so each 16-byte unit of that slot ends up holding the same unit of
+ * one of those rows (units of one slot, and its K and V, may come from
+ * different rows). Any head count and head_dim whose row is a multiple of 16
  * bytes (at most 1 MiB) is accepted; n_rows <= 2^25. Pools and rows 16-byte
  * aligned, slot_mapping 8-byte aligned. Asynchronous on `stream`; n_rows = 0
  * enqueues nothing.

@@ -61,8 +61,7 @@ def fill(lengths, budget: int, record: bool = True):
     Returns ``(workers used, pieces (w, b, lo, hi) in order)``, or
     ``(None, [])`` when the budget is below one tile plus a segment. The
     pieces are only listed when ``record`` is set."""
-    full = (budget - SEGMENT_COST) // TILE * TILE   # what a fresh worker takes of a longer rest
-    if full <= 0:
+    if (budget - SEGMENT_COST) // TILE <= 0:
         return None, []
     pieces = []
     w, room, used = 0, budget, 0
@@ -70,30 +69,22 @@ def fill(lengths, budget: int, record: bool = True):
         pos = 0
         while pos < n:
             rest = n - pos
-            if room == budget and rest > full:
-                # fresh workers, each taking `full` tokens, until the rest fits one
-                k = (rest - 1) // full
-                if record:
-                    pieces.extend((w + i, b, pos + i * full, pos + (i + 1) * full)
-                                  for i in range(k))
-                w += k
-                pos += k * full
-                used = w
-                continue
             if piece_cost(rest) <= room:
+                # the rest of the sequence fits the current worker whole
                 if record:
                     pieces.append((w, b, pos, n))
                 room -= piece_cost(rest)
                 used = w + 1
                 pos = n
-                continue
-            take = max(0, (room - SEGMENT_COST) // TILE * TILE)
-            if take:
-                if record:
-                    pieces.append((w, b, pos, pos + take))
-                used = w + 1
-                pos += take
-            w, room = w + 1, budget
+            else:
+                # the worker takes the whole tiles that fit, then is closed
+                take = max(0, (room - SEGMENT_COST) // TILE * TILE)
+                if take:
+                    if record:
+                        pieces.append((w, b, pos, pos + take))
+                    used = w + 1
+                    pos += take
+                w, room = w + 1, budget
     return used, pieces
 
 

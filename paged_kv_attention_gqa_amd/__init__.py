@@ -20,6 +20,7 @@ from ._build import LIB_PATH
 __all__ = [
     "PkvError", "Plan", "decode", "gather_mla", "library_path",
     "pkv_workspace_size", "pkv_plan_create", "pkv_plan_destroy", "pkv_plan_export",
+    "pkv_plan_workspace_size", "pkv_plan_upload",
     "pkv_run", "pkv_merge", "pkv_gather_mla_workspace_size", "pkv_gather_mla",
     "prepare_run", "prepare_merge",
     "pkv_block_table_workspace_size", "pkv_block_table_plan_create", "pkv_block_table_run",
@@ -48,6 +49,8 @@ SIGNATURES = {
     "pkv_plan_create": (_I32, [_I32P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _P, _SZ,
                                _P, _c.POINTER(_P)]),
     "pkv_plan_destroy": (None, [_P]),
+    "pkv_plan_workspace_size": (_I32, [_P, _c.POINTER(_SZ)]),
+    "pkv_plan_upload": (_I32, [_P, _P, _SZ, _P]),
     "pkv_plan_export": (_I32, [_P, _I32P, _SZ, _c.POINTER(_SZ)]),
     "pkv_run": (_I32, [_P, _P, _I32, _I32, _I32, _P, _P, _I64, _I32, _I32, _I32, _P, _I64, _P,
                        _I64, _c.c_float, _P, _SZ, _P, _P, _P]),
@@ -437,6 +440,18 @@ def _gather(fp8, q, kv_pool, indices, sm_scale, workspace, out, lse, d_v, stream
 
 # ------------------------------------------------------------ conveniences
 
+def pkv_plan_workspace_size(plan: Plan) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().pkv_plan_workspace_size(plan.handle, ctypes.byref(out)), "pkv_plan_workspace_size")
+    return int(out.value)
+
+
+def pkv_plan_upload(plan: Plan, workspace, stream=None) -> None:
+    _require(workspace, "workspace", (__import__("torch").uint8,))
+    _check(lib().pkv_plan_upload(plan.handle, _ptr(workspace), workspace.numel(), _stream(stream)),
+           "pkv_plan_upload")
+
+
 def decode(q, k_pool, v_pool, kv_indptr, kv_indices, sm_scale: Optional[float] = None,
            kv_indptr_host=None, allow_split=True, chunk_tokens=0, num_cus=0, stream=None):
     """Plan, run and merge one paged GQA decode; returns ``(out, lse)`` (bf16, fp32 base 2).
@@ -449,11 +464,10 @@ def decode(q, k_pool, v_pool, kv_indptr, kv_indices, sm_scale: Optional[float] =
         sm_scale = 1.0 / math.sqrt(q.shape[-1])
     if kv_indptr_host is None:
         kv_indptr_host = kv_indptr.cpu()
-    ws_bytes = pkv_workspace_size(kv_indptr_host, q.shape[1], k_pool.shape[2], q.shape[2],
-                                  k_pool.shape[1], num_cus, allow_split, chunk_tokens)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
     plan = pkv_plan_create(kv_indptr_host, q.shape[1], k_pool.shape[2], q.shape[2],
-                           k_pool.shape[1], num_cus, allow_split, chunk_tokens, ws, stream)
+                           k_pool.shape[1], num_cus, allow_split, chunk_tokens)
+    ws = torch.empty(max(pkv_plan_workspace_size(plan), 16), dtype=torch.uint8, device=q.device)
+    pkv_plan_upload(plan, ws, stream)
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
     pkv_run(plan, q, k_pool, v_pool, kv_indptr, kv_indices, sm_scale, ws, out, lse, stream)
@@ -473,13 +487,10 @@ def decode_block_table(q, k_pool, v_pool, block_table, seq_lens_host,
     import torch
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(q.shape[-1])
-    ws_bytes = pkv_block_table_workspace_size(seq_lens_host, q.shape[1], k_pool.shape[2],
-                                              q.shape[2], k_pool.shape[1], num_cus, allow_split,
-                                              chunk_tokens)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
     plan = pkv_block_table_plan_create(seq_lens_host, q.shape[1], k_pool.shape[2], q.shape[2],
-                                       k_pool.shape[1], num_cus, allow_split, chunk_tokens, ws,
-                                       stream)
+                                       k_pool.shape[1], num_cus, allow_split, chunk_tokens)
+    ws = torch.empty(max(pkv_plan_workspace_size(plan), 16), dtype=torch.uint8, device=q.device)
+    pkv_plan_upload(plan, ws, stream)
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
     pkv_block_table_run(plan, q, k_pool, v_pool, block_table, sm_scale, ws, out, lse, stream)

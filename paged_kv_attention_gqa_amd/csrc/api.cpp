@@ -4,6 +4,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <cmath>
 #include <cstdarg>
@@ -89,15 +90,27 @@ int32_t log2_exact(int32_t x) {
   return s;
 }
 
+// CU count of the current device, queried once per device.
+constexpr int kMaxDevices = 64;
+std::atomic<int32_t> g_device_cus[kMaxDevices];
+
 pkv_status resolve_cus(int32_t* num_cus) {
   if (*num_cus > 0) return PKV_OK;
   if (*num_cus < 0) return fail(PKV_ERR_INVALID_ARG, "num_cus must be >= 0");
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int32_t known = g_device_cus[dev].load(std::memory_order_relaxed);
+    if (known > 0) {
+      *num_cus = known;
+      return PKV_OK;
+    }
+  }
   int cus = 0;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "hipDeviceGetAttribute: %s", hipGetErrorString(e));
+  if (dev >= 0 && dev < kMaxDevices) g_device_cus[dev].store(cus, std::memory_order_relaxed);
   *num_cus = cus;
   return PKV_OK;
 }
@@ -139,27 +152,27 @@ pkv_status make_plan(const int32_t* kv_indptr_host, int32_t batch, int32_t num_q
   // * segment s: (b, tok_begin, tok_end, slot, token offset of sequence b,
   //   0, 0, 0), so page ids are found without reading kv_indptr;
   // * merge records (b, first_slot, n_segments, 0).
-  p->tables.clear();
-  p->tables.reserve(8 * (p->part.worker_ptr.size() + p->part.segments.size()) +
-                    4 * p->part.merges.size());
-  for (int32_t w = 0; w < p->part.n_workers; ++w) {
-    const int32_t sb = p->part.worker_ptr[static_cast<size_t>(w)];
-    const int32_t se = p->part.worker_ptr[static_cast<size_t>(w) + 1];
-    if (sb < se) {
-      const auto& sg = p->part.segments[static_cast<size_t>(sb)];
-      p->tables.insert(p->tables.end(),
-                       {sg.b, sg.tok_begin, sg.tok_end, sg.slot, kv_indptr_host[sg.b], sb, se, 0});
-    } else {
-      p->tables.insert(p->tables.end(), {0, 0, 0, -1, 0, sb, se, 0});
-    }
+  const pkv::Partition& pt = p->part;
+  const size_t n_workers = static_cast<size_t>(pt.n_workers);
+  const size_t n_segs = pt.segments.size();
+  p->tables.resize(8 * (n_workers + n_segs) + 4 * pt.merges.size());
+  int32_t* t = p->tables.data();
+  for (size_t w = 0; w < n_workers; ++w, t += 8) {
+    const int32_t sb = pt.worker_ptr[w];
+    const int32_t se = pt.worker_ptr[w + 1];
+    const pkv::Segment sg = sb < se ? pt.segments[static_cast<size_t>(sb)] : pkv::Segment{0, 0, 0, -1};
+    t[0] = sg.b; t[1] = sg.tok_begin; t[2] = sg.tok_end; t[3] = sg.slot;
+    t[4] = sb < se ? kv_indptr_host[sg.b] : 0; t[5] = sb; t[6] = se; t[7] = 0;
   }
-  const size_t n_wrec = 8 * static_cast<size_t>(p->part.n_workers);
-  for (const auto& sg : p->part.segments) {
-    p->tables.insert(p->tables.end(),
-                     {sg.b, sg.tok_begin, sg.tok_end, sg.slot, kv_indptr_host[sg.b], 0, 0, 0});
+  const size_t n_wrec = 8 * n_workers;
+  for (const auto& sg : pt.segments) {
+    t[0] = sg.b; t[1] = sg.tok_begin; t[2] = sg.tok_end; t[3] = sg.slot;
+    t[4] = kv_indptr_host[sg.b]; t[5] = 0; t[6] = 0; t[7] = 0;
+    t += 8;
   }
-  for (const auto& m : p->part.merges) {
-    p->tables.insert(p->tables.end(), {m.b, m.first_slot, m.n_segments, m.pad});
+  for (const auto& m : pt.merges) {
+    t[0] = m.b; t[1] = m.first_slot; t[2] = m.n_segments; t[3] = m.pad;
+    t += 4;
   }
   const size_t slots = static_cast<size_t>(p->part.n_slots);
   p->off_wptr = 0;
@@ -191,6 +204,24 @@ pkv_status offsets_from_lengths(const int32_t* seq_lens_host, int32_t batch,
   return PKV_OK;
 }
 
+// Checks the workspace and enqueues the copy of the plan's tables into it;
+// the plan is then bound to that workspace.
+pkv_status upload_plan(pkv_plan* p, void* workspace, size_t workspace_bytes, void* stream) {
+  if (workspace == nullptr) return fail(PKV_ERR_INVALID_ARG, "workspace is NULL");
+  if (workspace_bytes < p->ws_bytes)
+    return fail(PKV_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, plan needs %zu",
+                workspace_bytes, p->ws_bytes);
+  if (!aligned16(workspace)) return fail(PKV_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if (!p->tables.empty()) {
+    hipError_t e = hipMemcpyAsync(workspace, p->tables.data(), p->tables.size() * sizeof(int32_t),
+                                  hipMemcpyHostToDevice, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+      return fail(PKV_ERR_HIP, "uploading the plan tables: %s", hipGetErrorString(e));
+  }
+  p->workspace = workspace;
+  return PKV_OK;
+}
+
 // Shared by pkv_plan_create and pkv_block_table_plan_create.
 pkv_status create_plan(const int32_t* kv_indptr_host, int32_t batch, int32_t num_qo_heads,
                        int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
@@ -208,25 +239,11 @@ pkv_status create_plan(const int32_t* kv_indptr_host, int32_t batch, int32_t num
     return s;
   }
   if (workspace != nullptr) {
-    if (workspace_bytes < p->ws_bytes) {
-      const size_t need = p->ws_bytes;
+    s = upload_plan(p, workspace, workspace_bytes, stream);
+    if (s != PKV_OK) {
       delete p;
-      return fail(PKV_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, plan needs %zu",
-                  workspace_bytes, need);
+      return s;
     }
-    if (!aligned16(workspace)) {
-      delete p;
-      return fail(PKV_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-    }
-    if (!p->tables.empty()) {
-      hipError_t e = hipMemcpyAsync(workspace, p->tables.data(), p->tables.size() * sizeof(int32_t),
-                                    hipMemcpyHostToDevice, static_cast<hipStream_t>(stream));
-      if (e != hipSuccess) {
-        delete p;
-        return fail(PKV_ERR_HIP, "uploading the plan tables: %s", hipGetErrorString(e));
-      }
-    }
-    p->workspace = workspace;
   }
   *plan = p;
   return ok();
@@ -407,6 +424,18 @@ pkv_status pkv_block_table_plan_create(const int32_t* seq_lens_host, int32_t bat
 }
 
 void pkv_plan_destroy(pkv_plan* plan) { delete plan; }
+
+pkv_status pkv_plan_workspace_size(const pkv_plan* plan, size_t* bytes) {
+  if (plan == nullptr || bytes == nullptr) return fail(PKV_ERR_INVALID_ARG, "plan and bytes must be non-NULL");
+  *bytes = plan->ws_bytes;
+  return ok();
+}
+
+pkv_status pkv_plan_upload(pkv_plan* plan, void* workspace, size_t workspace_bytes, void* stream) {
+  if (plan == nullptr) return fail(PKV_ERR_INVALID_ARG, "plan is NULL");
+  const pkv_status s = upload_plan(plan, workspace, workspace_bytes, stream);
+  return s == PKV_OK ? ok() : s;
+}
 
 pkv_status pkv_plan_export(const pkv_plan* plan, int32_t* dst, size_t n_int32, size_t* needed) {
   if (plan == nullptr) return fail(PKV_ERR_INVALID_ARG, "plan is NULL");

@@ -2,6 +2,7 @@
 #include "plan.h"
 
 #include <algorithm>
+#include <climits>
 #include <numeric>
 
 namespace pkv {
@@ -24,7 +25,7 @@ struct Piece {
 // of workers used (-1 if the budget cannot hold one tile and a segment) and,
 // if `pieces` is given, the pieces in order.
 int64_t greedy_fill(const int32_t* kv_indptr, int32_t batch, int64_t budget,
-                    std::vector<Piece>* pieces) {
+                    std::vector<Piece>* pieces, int64_t stop_above = INT64_MAX) {
   const int64_t full = (budget - kSegmentCost) / kTile * kTile;   // budget >= 0
   if (full <= 0) return -1;
   if (pieces) pieces->clear();
@@ -45,6 +46,7 @@ int64_t greedy_fill(const int32_t* kv_indptr, int32_t batch, int64_t budget,
         w += k;
         pos += k * full;
         used = w;
+        if (used > stop_above) return used;
         continue;
       }
       if (piece_cost(rest) <= room) {
@@ -63,6 +65,7 @@ int64_t greedy_fill(const int32_t* kv_indptr, int32_t batch, int64_t budget,
       }
       ++w;
       room = budget;
+      if (w > stop_above) return w;
     }
   }
   return used;
@@ -118,27 +121,47 @@ bool build_partition(const int32_t* kv_indptr, int32_t batch, int32_t num_cus,
     limit = std::min<int64_t>(int64_t(num_cus) * kWorkersPerCu, cdiv(total, kMinWorkerTokens));
   }
   std::vector<Piece> pieces;
+  pieces.reserve(static_cast<size_t>(batch) + static_cast<size_t>(std::max<int64_t>(limit, 0)) + 1);
   int64_t workers = 0;
   if (limit > 0) {
-    // Smallest budget whose greedy fill needs at most `limit` workers; the
-    // sum of the whole sequences' costs always fits one worker.
-    int64_t lo = kTile + kSegmentCost, hi = 0;
+    // Smallest budget whose greedy fill needs at most `limit` workers. Every
+    // cost is a multiple of kTile, so the fill depends on the budget only
+    // through budget / kTile, and the smallest fitting budget is a multiple of
+    // kTile: search over m = budget / kTile. Needing fewer workers as the
+    // budget grows, the fill fits no m below the even share of the whole
+    // sequences' costs (cuts only add cost), and the sum of those costs fits
+    // one worker. Gallop up from the even share, then bisect.
+    int64_t total_cost = 0;
     for (int32_t b = 0; b < batch; ++b) {
       const int64_t n = kv_indptr[b + 1] - kv_indptr[b];
-      if (n > 0) hi += piece_cost(n);
+      if (n > 0) total_cost += piece_cost(n);
     }
-    hi = std::max(hi, lo);
+    const int64_t m_min = (kTile + kSegmentCost) / kTile;
+    const int64_t m_max = std::max(m_min, total_cost / kTile);
+    auto fits = [&](int64_t m) {
+      const int64_t used = greedy_fill(kv_indptr, batch, m * kTile, nullptr, limit);
+      return used >= 0 && used <= limit;
+    };
+    int64_t lo = std::min(m_max, std::max(m_min, cdiv(total_cost, kTile * limit)));
+    int64_t hi = lo;
+    for (int64_t step = 1; !fits(hi); step *= 2) {
+      lo = hi + 1;
+      hi = std::min(m_max, hi + step);
+    }
     while (lo < hi) {
       const int64_t mid = lo + (hi - lo) / 2;
-      const int64_t used = greedy_fill(kv_indptr, batch, mid, nullptr);
-      if (used >= 0 && used <= limit) hi = mid;
+      if (fits(mid)) hi = mid;
       else lo = mid + 1;
     }
-    workers = greedy_fill(kv_indptr, batch, lo, &pieces);
+    workers = greedy_fill(kv_indptr, batch, lo * kTile, &pieces);
   }
   p.n_workers = static_cast<int32_t>(workers);
 
-  std::vector<std::vector<Segment>> per_worker(static_cast<size_t>(workers));
+  // The fill emits pieces in worker order, which is also sequence order, so
+  // segments are written in one pass and grouped by worker already.
+  p.segments.reserve(pieces.size());
+  p.merges.reserve(static_cast<size_t>(batch));
+  p.worker_ptr.assign(static_cast<size_t>(workers) + 1, 0);
   int32_t slot = 0;
   size_t i = 0;
   for (int32_t b = 0; b < batch; ++b) {
@@ -150,8 +173,9 @@ bool build_partition(const int32_t* kv_indptr, int32_t batch, int32_t num_cus,
     while (j < pieces.size() && pieces[j].b == b) ++j;
     const int32_t k = static_cast<int32_t>(j - i);
     for (size_t x = i; x < j; ++x) {
-      per_worker[static_cast<size_t>(pieces[x].w)].push_back(
+      p.segments.push_back(
           {b, pieces[x].lo, pieces[x].hi, k == 1 ? -1 : slot + static_cast<int32_t>(x - i)});
+      ++p.worker_ptr[static_cast<size_t>(pieces[x].w) + 1];
     }
     if (k > 1) {
       p.merges.push_back({b, slot, k, 0});
@@ -159,12 +183,8 @@ bool build_partition(const int32_t* kv_indptr, int32_t batch, int32_t num_cus,
     }
     i = j;
   }
+  for (size_t w = 1; w < p.worker_ptr.size(); ++w) p.worker_ptr[w] += p.worker_ptr[w - 1];
   p.n_slots = slot;
-  p.worker_ptr.push_back(0);
-  for (auto& segs : per_worker) {
-    p.segments.insert(p.segments.end(), segs.begin(), segs.end());
-    p.worker_ptr.push_back(static_cast<int32_t>(p.segments.size()));
-  }
   *out = std::move(p);
   return true;
 }

@@ -38,7 +38,7 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_symbols()
-    assert len(names) == 15
+    assert len(names) == 17
     for name in names:
         assert hasattr(lib, name), name
         assert name in pkv.SIGNATURES, name
@@ -102,6 +102,35 @@ def test_workspace_size_formula(lib):
     part_o = al(tables)
     part_lse = al(part_o + slots * 32 * 128 * 4)
     assert n == al(part_lse + slots * 32 * 4)
+
+
+@pytest.mark.parametrize("lengths", [[1000, 10, 0, 5000], [], [0, 0], [17, 64], [4096] * 70])
+def test_plan_workspace_size_matches(lib, lengths):
+    """A host-only plan reports the workspace size pkv_workspace_size gives for
+    its batch, and rejects uploads into a workspace that is too small, NULL or
+    misaligned before any HIP call."""
+    ind = _indptr(lengths)
+    st, n = _ws(ind)
+    assert st == pkv.PKV_OK
+    plan = pkv.pkv_plan_create(ind, num_cus=256)
+    assert pkv.pkv_plan_workspace_size(plan) == n
+    up = pkv.lib().pkv_plan_upload
+    if n:
+        assert up(plan.handle, FAKE, n - 16, 0) == pkv.PKV_ERR_WORKSPACE_TOO_SMALL
+        assert up(plan.handle, FAKE + 4, n, 0) == pkv.PKV_ERR_INVALID_ARG
+    assert up(plan.handle, None, n, 0) == pkv.PKV_ERR_INVALID_ARG
+    assert up(None, FAKE, n, 0) == pkv.PKV_ERR_INVALID_ARG
+    out = ctypes.c_size_t(0)
+    assert pkv.lib().pkv_plan_workspace_size(None, ctypes.byref(out)) == pkv.PKV_ERR_INVALID_ARG
+
+
+def test_sm_scale_any_finite_value(lib):
+    """Zero and negative scales pass the argument checks (the attention is
+    defined for every real scale); the call then stops at the host-only plan."""
+    ind = _indptr([17, 64])
+    h = pkv.pkv_plan_create(ind, num_cus=256).handle
+    for scale in (0.0, -0.5, -1e30, 1e30):
+        assert _run_raw(h, scale=scale) == pkv.PKV_ERR_PLAN_MISMATCH
 
 
 def _host_plan(ind, cus, split, chunk):

@@ -71,9 +71,11 @@ def test_append_nothing():
     assert np.array_equal(got[0], k_pool) and np.array_equal(got[1], v_pool)
 
 
-def test_append_duplicate_slots_hold_one_of_the_rows():
-    """Two rows with one slot race; the slot must hold one whole row (K and V
-    of the same row are not promised together), every other slot as the oracle."""
+def test_append_duplicate_slots_hold_pieces_of_the_rows():
+    """Rows that name the same slot race, and nothing orders their stores, so
+    only each 16-byte unit of the slot is promised: it holds the same unit of
+    one of the rows that name the slot (the units of a slot, and K and V, may
+    come from different rows). Every other slot is as the oracle has it."""
     rng = np.random.default_rng(4)
     k_pool = random_bits(rng, (8, 16, 4, 128))
     v_pool = random_bits(rng, (8, 16, 4, 128))
@@ -85,8 +87,13 @@ def test_append_duplicate_slots_hold_one_of_the_rows():
     flat_v = got_v.reshape(-1, 4, 128)
     for slot in (17, 40):
         cand = np.nonzero(slots == slot)[0]
-        assert any(np.array_equal(flat_k[slot], rows_k[i]) for i in cand)
-        assert any(np.array_equal(flat_v[slot], rows_v[i]) for i in cand)
+        for got, rows in ((flat_k[slot], rows_k), (flat_v[slot], rows_v)):
+            units = got.reshape(-1, 8)                     # 16-byte units of the 1 KB row
+            options = [rows[i].reshape(-1, 8) for i in cand]
+            ok = np.zeros(units.shape[0], bool)
+            for o in options:
+                ok |= np.all(units == o, axis=1)
+            assert ok.all(), f"slot {slot}: a 16-byte unit matches none of its rows"
     unique = [i for i in range(6) if (slots == slots[i]).sum() == 1]
     want_k, want_v = ref.kv_append(k_pool, v_pool, rows_k[unique], rows_v[unique], slots[unique])
     other = np.ones(8 * 16, bool)

@@ -263,6 +263,25 @@ pkv_status pkv_gather_mla(const void* q, const void* kv_pool, int64_t pool_token
                           size_t workspace_bytes, void* out, float* lse, void* stream);
 
 /*
+ * The bf16 gather above without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops that
+ * forbid allocation). Same arguments as pkv_gather_mla minus the workspace;
+ * same results, bit for bit. The fp32 partials live in a device array the
+ * library holds on each GPU it runs on (48 MiB, kept until the process ends),
+ * found on the first call with that GPU current. A shape whose partials need
+ * more than that (pkv_gather_mla_workspace_size bytes > 48 MiB) returns
+ * PKV_ERR_UNSUPPORTED before any HIP call. The call allocates nothing. Every
+ * call on one GPU shares its scratch: calls that overlap in time on one GPU
+ * (different streams, or threads without ordering) race and may return wrong
+ * results; calls ordered on one stream do not.
+ */
+pkv_status pkv_gather_mla_noalloc(const void* q, const void* kv_pool, int64_t pool_tokens,
+                                  const int32_t* indices, int32_t topk, int32_t batch,
+                                  int32_t num_qo_heads, int32_t d_qk, int32_t d_v, float sm_scale,
+                                  const float* attn_sink, const int32_t* topk_length, void* out,
+                                  float* lse, void* stream);
+
+/*
  * The same gather over a pool of FP8 latent tokens (FlagGems
  * flash_mla_with_kvcache page, FP8 sparse mode): kv_pool is
  * [pool_tokens, 656] bytes per token: 512 OCP e4m3 ("e4m3fn") values, then 4

@@ -25,7 +25,7 @@ __all__ = [
     "prepare_run", "prepare_merge",
     "pkv_block_table_workspace_size", "pkv_block_table_plan_create", "pkv_block_table_run",
     "prepare_block_table_run", "decode_block_table", "pkv_append_kv",
-    "pkv_gather_mla_fp8", "gather_mla_fp8",
+    "pkv_gather_mla_fp8", "gather_mla_fp8", "pkv_gather_mla_noalloc",
     "pkv_status_string", "pkv_last_error",
 ]
 
@@ -65,6 +65,8 @@ SIGNATURES = {
     "pkv_gather_mla_workspace_size": (_I32, [_I32, _I32, _I32, _I32, _I32, _c.POINTER(_SZ)]),
     "pkv_gather_mla": (_I32, [_P, _P, _I64, _P, _I32, _I32, _I32, _I32, _I32, _c.c_float, _P,
                               _P, _P, _SZ, _P, _P, _P]),
+    "pkv_gather_mla_noalloc": (_I32, [_P, _P, _I64, _P, _I32, _I32, _I32, _I32, _I32,
+                                      _c.c_float, _P, _P, _P, _P, _P]),
     "pkv_gather_mla_fp8": (_I32, [_P, _P, _I64, _P, _I32, _I32, _I32, _I32, _I32, _c.c_float,
                                   _P, _P, _P, _SZ, _P, _P, _P]),
     "pkv_status_string": (_c.c_char_p, [_I32]),
@@ -399,6 +401,13 @@ def pkv_gather_mla(q, kv_pool, indices, sm_scale, workspace, out, lse, d_v=512, 
             topk_length)
 
 
+def pkv_gather_mla_noalloc(q, kv_pool, indices, sm_scale, out, lse, d_v=512, stream=None,
+                           attn_sink=None, topk_length=None):
+    """pkv_gather_mla with the partials in the library's device scratch (no workspace)."""
+    _gather(False, q, kv_pool, indices, sm_scale, None, out, lse, d_v, stream, attn_sink,
+            topk_length, noalloc=True)
+
+
 def pkv_gather_mla_fp8(q, kv_pool, indices, sm_scale, workspace, out, lse, d_v=512, stream=None,
                        attn_sink=None, topk_length=None):
     """Like pkv_gather_mla over a uint8 pool of 656-byte FP8 tokens ``[T, 656]``."""
@@ -407,7 +416,7 @@ def pkv_gather_mla_fp8(q, kv_pool, indices, sm_scale, workspace, out, lse, d_v=5
 
 
 def _gather(fp8, q, kv_pool, indices, sm_scale, workspace, out, lse, d_v, stream, attn_sink,
-            topk_length):
+            topk_length, noalloc=False):
     import torch
     bf = _bf16_types()
     _require(q, "q", bf)
@@ -429,6 +438,12 @@ def _gather(fp8, q, kv_pool, indices, sm_scale, workspace, out, lse, d_v, stream
         raise ValueError(f"kv_pool rows must have {width} elements and indices one row per query")
     if tuple(out.shape) != (q.shape[0], q.shape[1], d_v) or tuple(lse.shape) != tuple(q.shape[:2]):
         raise ValueError("out must be [B, Hq, d_v] and lse [B, Hq]")
+    if noalloc:
+        _check(lib().pkv_gather_mla_noalloc(
+            _ptr(q), _ptr(kv_pool), kv_pool.shape[0], _ptr(indices), indices.shape[1],
+            q.shape[0], q.shape[1], q.shape[2], d_v, float(sm_scale), _ptr(attn_sink),
+            _ptr(topk_length), _ptr(out), _ptr(lse), _stream(stream)), "pkv_gather_mla_noalloc")
+        return
     ws_bytes = 0 if workspace is None else workspace.numel()
     fn = lib().pkv_gather_mla_fp8 if fp8 else lib().pkv_gather_mla
     _check(fn(_ptr(q), _ptr(kv_pool), kv_pool.shape[0], _ptr(indices),

@@ -583,6 +583,30 @@ pkv_status pkv_gather_mla(const void* q, const void* kv_pool, int64_t pool_token
                        lse, stream);
 }
 
+pkv_status pkv_gather_mla_noalloc(const void* q, const void* kv_pool, int64_t pool_tokens,
+                                  const int32_t* indices, int32_t topk, int32_t batch,
+                                  int32_t num_qo_heads, int32_t d_qk, int32_t d_v, float sm_scale,
+                                  const float* attn_sink, const int32_t* topk_length, void* out,
+                                  float* lse, void* stream) {
+  std::string err;
+  size_t need = 0;
+  const int code = pkv::mla_workspace_bytes(batch, num_qo_heads, d_qk, d_v, topk, &need, &err);
+  if (code != 0) return fail(static_cast<pkv_status>(code), "%s", err.c_str());
+  if (need > pkv::kMlaScratchBytes)
+    return fail(PKV_ERR_UNSUPPORTED,
+                "this gather needs %zu bytes of partials; the library's device scratch holds %zu "
+                "(use pkv_gather_mla with a workspace)",
+                need, pkv::kMlaScratchBytes);
+  void* scratch = nullptr;
+  if (need > 0 && batch > 0) {
+    const hipError_t e = pkv::mla_scratch(&scratch);
+    if (e != hipSuccess)
+      return fail(PKV_ERR_HIP, "locating the device scratch: %s", hipGetErrorString(e));
+  }
+  return gather_common(q, kv_pool, false, pool_tokens, indices, topk, batch, num_qo_heads, d_qk,
+                       d_v, sm_scale, attn_sink, topk_length, scratch, need, out, lse, stream);
+}
+
 pkv_status pkv_gather_mla_fp8(const void* q, const void* kv_pool, int64_t pool_tokens,
                               const int32_t* indices, int32_t topk, int32_t batch,
                               int32_t num_qo_heads, int32_t d_qk, int32_t d_v, float sm_scale,

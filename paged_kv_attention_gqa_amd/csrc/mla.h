@@ -20,6 +20,15 @@ constexpr int kMlaFp8TokenBytes = 656;
 // that the workspace size depends on the shape only.
 constexpr int kMlaPlanCus = 256;
 
+// Device scratch held by the library for pkv_gather_mla_noalloc: one array of
+// this many bytes per GPU, alive until the process ends (48 MiB: the fp32
+// partials of a batch of 32 rows x 128 heads cut into 4 pieces take 33.6 MB).
+constexpr size_t kMlaScratchBytes = size_t(48) << 20;
+
+// Address of this library's device scratch on the current device, looked up
+// (hipGetSymbolAddress) on the first call made with that device current.
+hipError_t mla_scratch(void** ptr);
+
 // Checks the gather shape; returns 0 and the workspace size, or a pkv_status
 // code with a message.
 int mla_workspace_bytes(int32_t batch, int32_t num_qo_heads, int32_t d_qk, int32_t d_v,

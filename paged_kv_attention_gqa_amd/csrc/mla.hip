@@ -52,6 +52,8 @@
 //   the LSE stays that of the entries alone, as the page stores it.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "mla.h"
 
 namespace pkv {
@@ -465,7 +467,31 @@ int mla_pieces(int32_t batch, int32_t num_qo_heads, int32_t topk, int num_cus) {
   return min(pieces, max_pieces);
 }
 
+// The fp32 partials of pkv_gather_mla_noalloc. In host code this name only
+// stands for the array: kernels get its device address from mla_scratch.
+static __device__ __align__(256) unsigned char scratch[kMlaScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
 }  // namespace
+
+hipError_t mla_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 int mla_workspace_bytes(int32_t batch, int32_t num_qo_heads, int32_t d_qk, int32_t d_v,
                         int32_t topk, size_t* bytes, std::string* err) {

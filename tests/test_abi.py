@@ -38,7 +38,7 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_symbols()
-    assert len(names) == 17
+    assert len(names) == 18
     for name in names:
         assert hasattr(lib, name), name
         assert name in pkv.SIGNATURES, name
@@ -122,6 +122,18 @@ def test_plan_workspace_size_matches(lib, lengths):
     assert up(None, FAKE, n, 0) == pkv.PKV_ERR_INVALID_ARG
     out = ctypes.c_size_t(0)
     assert pkv.lib().pkv_plan_workspace_size(None, ctypes.byref(out)) == pkv.PKV_ERR_INVALID_ARG
+
+
+def test_noalloc_gather_rejects_a_batch_beyond_the_scratch(lib):
+    """100 rows x 128 heads cut into 2 pieces need 52.5 MB of partials, more
+    than the library's 48 MiB device scratch: refused before any HIP call."""
+    need = pkv.pkv_gather_mla_workspace_size(100, 128, 576, 512, 2048)
+    assert need > 48 << 20
+    st = lib.pkv_gather_mla_noalloc(FAKE, FAKE, 1, FAKE, 2048, 100, 128, 576, 512, 0.04, None,
+                                    None, FAKE, FAKE, None)
+    assert st == pkv.PKV_ERR_UNSUPPORTED and "scratch" in pkv.pkv_last_error()
+    assert lib.pkv_gather_mla_noalloc(FAKE, FAKE, 1, FAKE, 2048, 2, 128, 576, 500, 0.04, None,
+                                      None, FAKE, FAKE, None) == pkv.PKV_ERR_UNSUPPORTED
 
 
 def test_sm_scale_any_finite_value(lib):

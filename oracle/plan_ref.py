@@ -12,7 +12,8 @@ exact rule is this library's own and is stated here once:
 * The batch's ``N = kv_indptr[B]`` tokens go, sequence by sequence in order,
   to at most ``W`` workers, ``W = ceil(N / chunk_tokens)`` when
   ``chunk_tokens > 0``, else ``min(num_cus * WORKERS_PER_CU,
-  ceil(N / MIN_WORKER_TOKENS))``; no workers when ``N = 0``. A piece of ``n``
+  max(ceil(N / MIN_WORKER_TOKENS), non-empty sequences))``; no workers when
+  ``N = 0``. A piece of ``n``
   tokens of one sequence costs ``ceil(n / TILE) * TILE + SEGMENT_COST`` (its
   tiles, plus one tile's worth for starting a segment). Workers are filled
   greedily with a cost budget ``C``: the rest of the current sequence goes to
@@ -106,7 +107,8 @@ def make_plan(kv_indptr, num_cus: int, allow_split: bool = True, chunk_tokens: i
     elif chunk_tokens > 0:
         limit = _cdiv(total, chunk_tokens)
     else:
-        limit = min(num_cus * WORKERS_PER_CU, _cdiv(total, MIN_WORKER_TOKENS))
+        nonempty = sum(1 for n in lengths if n > 0)
+        limit = min(num_cus * WORKERS_PER_CU, max(_cdiv(total, MIN_WORKER_TOKENS), nonempty))
     pieces = []
     if limit:
         lo = TILE + SEGMENT_COST

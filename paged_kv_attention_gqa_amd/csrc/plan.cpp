@@ -118,7 +118,13 @@ bool build_partition(const int32_t* kv_indptr, int32_t batch, int32_t num_cus,
   } else if (chunk_tokens > 0) {
     limit = cdiv(total, chunk_tokens);
   } else {
-    limit = std::min<int64_t>(int64_t(num_cus) * kWorkersPerCu, cdiv(total, kMinWorkerTokens));
+    // Short batches are latency-bound: each non-empty sequence may have a
+    // worker of its own even when that leaves fewer than kMinWorkerTokens
+    // tokens per worker.
+    int64_t nonempty = 0;
+    for (int32_t b = 0; b < batch; ++b) nonempty += kv_indptr[b + 1] > kv_indptr[b];
+    limit = std::min<int64_t>(int64_t(num_cus) * kWorkersPerCu,
+                              std::max(cdiv(total, kMinWorkerTokens), nonempty));
   }
   std::vector<Piece> pieces;
   pieces.reserve(static_cast<size_t>(batch) + static_cast<size_t>(std::max<int64_t>(limit, 0)) + 1);

@@ -50,10 +50,10 @@ struct Partition {
 
 // Checks kv_indptr (starts at 0, non-decreasing) and builds the partition.
 // allow_split = false gives one worker per sequence. chunk_tokens > 0 sets
-// the most workers to ceil(N / chunk_tokens); 0 to num_cus * kWorkersPerCu
-// (fewer when the batch has under kMinWorkerTokens tokens per worker); the
-// fill may use fewer. Returns false
-// with a message in *err on bad input.
+// the most workers to ceil(N / chunk_tokens); 0 to num_cus * kWorkersPerCu,
+// or fewer for a short batch: max(ceil(N / kMinWorkerTokens), number of
+// non-empty sequences). The fill may use fewer. Returns false with a message
+// in *err on bad input.
 bool build_partition(const int32_t* kv_indptr, int32_t batch, int32_t num_cus,
                      bool allow_split, int32_t chunk_tokens, Partition* out, std::string* err);
 

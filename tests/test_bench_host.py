@@ -19,11 +19,11 @@ def test_more_than_one_gpu_is_refused():
 
 
 def test_algorithmic_bytes_by_hand():
-    # tiny: two sequences of 17 and 64 tokens inside one worker, written directly
+    # tiny: two sequences of 17 and 64 tokens, one worker each, written directly
     w = make_config("tiny")
     flat = pkv.pkv_plan_export(pkv.pkv_plan_create(w.kv_indptr, num_cus=256))
     n_workers, n_segs, _, n_slots = flat[:4]
-    assert (n_workers, n_segs, n_slots) == (1, 2, 0)
+    assert (n_workers, n_segs, n_slots) == (2, 2, 0)
     want = 2048 * 81 + 4 * 81 + 8192 * 2 + 2 * (8192 + 128) + 32 * 2
     assert bench.algorithmic_decode_bytes(w, flat) == want
 

@@ -75,7 +75,7 @@ def test_ragged_small(lengths, chunk):
 
 def test_many_short_sequences_per_worker():
     """3,000 sequences of 0-4 tokens and one of 5,000: the cost-balanced plan
-    packs a few dozen short segments into a worker, and the long sequence is
+    packs about ten short segments into a worker, and the long sequence is
     cut across workers."""
     rng = np.random.default_rng(230)
     lengths = [int(x) for x in rng.integers(0, 5, size=3000)]
@@ -83,7 +83,7 @@ def test_many_short_sequences_per_worker():
     w = make_gqa(231, lengths, pool_pages=sum(lengths) + 11)
     plan = pkv.pkv_plan_create(w.kv_indptr, num_cus=256)
     flat = pkv.pkv_plan_export(plan)
-    assert max(np.diff(flat[4:5 + flat[0]])) > 20 and flat[3] > 1
+    assert max(np.diff(flat[4:5 + flat[0]])) >= 8 and flat[3] > 1
     want = ref.gqa_paged_decode(w.q, w.k_pool, w.v_pool, w.kv_indptr, w.kv_indices, w.sm_scale)
     check(w, want, run_gpu(w), "many short sequences")
 

@@ -47,7 +47,9 @@ def _check(indptr, num_cus, allow_split, chunk_tokens):
         # tile plus a segment
         assert all(c > budget - tile - seg for c in costs[:-1])
         limit = (-(-total // chunk_tokens) if chunk_tokens > 0
-                 else min(num_cus * plan_ref.WORKERS_PER_CU, -(-total // plan_ref.MIN_WORKER_TOKENS)))
+                 else min(num_cus * plan_ref.WORKERS_PER_CU,
+                          max(-(-total // plan_ref.MIN_WORKER_TOKENS),
+                              sum(1 for b in range(batch) if indptr[b + 1] > indptr[b]))))
         assert len(per_worker) <= limit
         # the budget is the smallest that fits: one less needs more workers
         if budget > tile + seg:

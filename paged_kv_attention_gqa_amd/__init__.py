@@ -22,7 +22,7 @@ __all__ = [
     "pkv_workspace_size", "pkv_plan_create", "pkv_plan_destroy", "pkv_plan_export",
     "pkv_plan_workspace_size", "pkv_plan_upload",
     "pkv_run", "pkv_merge", "pkv_gather_mla_workspace_size", "pkv_gather_mla",
-    "prepare_run", "prepare_merge",
+    "prepare_run", "prepare_merge", "prepare_gather_mla", "prepare_append_kv",
     "pkv_block_table_workspace_size", "pkv_block_table_plan_create", "pkv_block_table_run",
     "prepare_block_table_run", "decode_block_table", "pkv_append_kv",
     "pkv_gather_mla_fp8", "gather_mla_fp8", "pkv_gather_mla_noalloc",
@@ -369,6 +369,23 @@ def pkv_merge(plan: Plan, workspace, out, lse, stream=None):
 def pkv_append_kv(k_pool, v_pool, k_rows, v_rows, slot_mapping, stream=None):
     """Store k_rows / v_rows ``[n, Hkv, D]`` at the int64 ``slot_mapping`` positions
     of the pools ``[pages, page_size, Hkv, D]`` (slots outside the pool are skipped)."""
+    _check(lib().pkv_append_kv(*_append_args(k_pool, v_pool, k_rows, v_rows, slot_mapping,
+                                             stream)), "pkv_append_kv")
+
+
+def prepare_append_kv(k_pool, v_pool, k_rows, v_rows, slot_mapping, stream=None):
+    """Like prepare_run, for pkv_append_kv."""
+    args = _append_args(k_pool, v_pool, k_rows, v_rows, slot_mapping, stream)
+    fn = lib().pkv_append_kv
+
+    def call():
+        st = fn(*args)
+        if st != PKV_OK:
+            _check(st, "pkv_append_kv")
+    return call
+
+
+def _append_args(k_pool, v_pool, k_rows, v_rows, slot_mapping, stream):
     import torch
     bf = _bf16_types()
     for t, name in ((k_pool, "k_pool"), (v_pool, "v_pool"), (k_rows, "k_rows"),
@@ -381,10 +398,8 @@ def pkv_append_kv(k_pool, v_pool, k_rows, v_rows, slot_mapping, stream=None):
     want = (n, k_pool.shape[2], k_pool.shape[3])
     if tuple(k_rows.shape) != want or tuple(v_rows.shape) != want:
         raise ValueError(f"k_rows and v_rows must be {list(want)}")
-    _check(lib().pkv_append_kv(_ptr(k_pool), _ptr(v_pool), k_pool.shape[0], k_pool.shape[1],
-                               k_pool.shape[2], k_pool.shape[3], _ptr(k_rows), _ptr(v_rows),
-                               _ptr(slot_mapping), n, _stream(stream)),
-           "pkv_append_kv")
+    return (_ptr(k_pool), _ptr(v_pool), k_pool.shape[0], k_pool.shape[1], k_pool.shape[2],
+            k_pool.shape[3], _ptr(k_rows), _ptr(v_rows), _ptr(slot_mapping), n, _stream(stream))
 
 
 def pkv_gather_mla_workspace_size(batch, num_qo_heads, d_qk, d_v, topk) -> int:
@@ -417,6 +432,28 @@ def pkv_gather_mla_fp8(q, kv_pool, indices, sm_scale, workspace, out, lse, d_v=5
 
 def _gather(fp8, q, kv_pool, indices, sm_scale, workspace, out, lse, d_v, stream, attn_sink,
             topk_length, noalloc=False):
+    fn, args, name = _gather_args(fp8, q, kv_pool, indices, sm_scale, workspace, out, lse, d_v,
+                                  stream, attn_sink, topk_length, noalloc)
+    _check(fn(*args), name)
+
+
+def prepare_gather_mla(q, kv_pool, indices, sm_scale, workspace, out, lse, d_v=512, stream=None,
+                       attn_sink=None, topk_length=None, fp8=False, noalloc=False):
+    """Marshal a pkv_gather_mla (or _fp8 / _noalloc) call once; the returned
+    callable enqueues the same call again with no per-call checks in Python.
+    The tensors must stay alive and in place while the callable is used."""
+    fn, args, name = _gather_args(fp8, q, kv_pool, indices, sm_scale, workspace, out, lse, d_v,
+                                  stream, attn_sink, topk_length, noalloc)
+
+    def call():
+        st = fn(*args)
+        if st != PKV_OK:
+            _check(st, name)
+    return call
+
+
+def _gather_args(fp8, q, kv_pool, indices, sm_scale, workspace, out, lse, d_v, stream, attn_sink,
+                 topk_length, noalloc=False):
     import torch
     bf = _bf16_types()
     _require(q, "q", bf)
@@ -439,18 +476,18 @@ def _gather(fp8, q, kv_pool, indices, sm_scale, workspace, out, lse, d_v, stream
     if tuple(out.shape) != (q.shape[0], q.shape[1], d_v) or tuple(lse.shape) != tuple(q.shape[:2]):
         raise ValueError("out must be [B, Hq, d_v] and lse [B, Hq]")
     if noalloc:
-        _check(lib().pkv_gather_mla_noalloc(
-            _ptr(q), _ptr(kv_pool), kv_pool.shape[0], _ptr(indices), indices.shape[1],
-            q.shape[0], q.shape[1], q.shape[2], d_v, float(sm_scale), _ptr(attn_sink),
-            _ptr(topk_length), _ptr(out), _ptr(lse), _stream(stream)), "pkv_gather_mla_noalloc")
-        return
+        return (lib().pkv_gather_mla_noalloc,
+                (_ptr(q), _ptr(kv_pool), kv_pool.shape[0], _ptr(indices), indices.shape[1],
+                 q.shape[0], q.shape[1], q.shape[2], d_v, float(sm_scale), _ptr(attn_sink),
+                 _ptr(topk_length), _ptr(out), _ptr(lse), _stream(stream)),
+                "pkv_gather_mla_noalloc")
     ws_bytes = 0 if workspace is None else workspace.numel()
     fn = lib().pkv_gather_mla_fp8 if fp8 else lib().pkv_gather_mla
-    _check(fn(_ptr(q), _ptr(kv_pool), kv_pool.shape[0], _ptr(indices),
-                                indices.shape[1], q.shape[0], q.shape[1], q.shape[2], d_v,
-                                float(sm_scale), _ptr(attn_sink), _ptr(topk_length),
-                                _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse), _stream(stream)),
-           "pkv_gather_mla_fp8" if fp8 else "pkv_gather_mla")
+    return (fn, (_ptr(q), _ptr(kv_pool), kv_pool.shape[0], _ptr(indices), indices.shape[1],
+                 q.shape[0], q.shape[1], q.shape[2], d_v, float(sm_scale), _ptr(attn_sink),
+                 _ptr(topk_length), _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse),
+                 _stream(stream)),
+            "pkv_gather_mla_fp8" if fp8 else "pkv_gather_mla")
 
 
 # ------------------------------------------------------------ conveniences

@@ -105,14 +105,19 @@ struct StagedBf16 {
     return u * kThreadsPerRow + static_cast<int>(threadIdx.x % kThreadsPerRow) < kUnitsPerRow;
   }
 
-  __device__ __forceinline__ void load(int32_t id, int64_t pool_tokens, const void* kv) {
+  // Every load is issued, so the compiler can count the loads in flight: a
+  // masked entry reads the in-bounds row `safe` instead (never stored, so
+  // never used), and the fifth unit of threads past the row's end re-reads
+  // the row's last unit.
+  __device__ __forceinline__ void load(int32_t id, int64_t pool_tokens, const void* kv,
+                                       const void* safe) {
     valid = id >= 0 && static_cast<int64_t>(id) < pool_tokens;
-    if (!valid) return;
-    const uint16_t* src = static_cast<const uint16_t*>(kv) + static_cast<int64_t>(id) * kMlaDqk +
-                          (threadIdx.x % kThreadsPerRow) * 8;
+    const uint16_t* row = valid ? static_cast<const uint16_t*>(kv) + static_cast<int64_t>(id) * kMlaDqk
+                                : static_cast<const uint16_t*>(safe);
+    const int j = static_cast<int>(threadIdx.x % kThreadsPerRow);
 #pragma unroll
     for (int u = 0; u < kLoadsPerThread; ++u)
-      if (has_unit(u)) v[u] = *reinterpret_cast<const u32x4*>(src + u * kThreadsPerRow * 8);
+      v[u] = *reinterpret_cast<const u32x4*>(row + min(j + u * kThreadsPerRow, kUnitsPerRow - 1) * 8);
   }
 
   // A masked row is not stored; only its flag is cleared.
@@ -139,15 +144,18 @@ struct StagedFp8 {
   u32x4 tail;
   bool valid;
 
-  __device__ __forceinline__ void load(int32_t id, int64_t pool_tokens, const void* kv) {
+  // As for bf16 rows, every load is issued (masked entries read `safe`;
+  // threads j >= 8 re-read a tail unit they do not store).
+  __device__ __forceinline__ void load(int32_t id, int64_t pool_tokens, const void* kv,
+                                       const void* safe) {
     valid = id >= 0 && static_cast<int64_t>(id) < pool_tokens;
-    if (!valid) return;
     const int j = threadIdx.x % kThreadsPerRow;
-    const uint8_t* src = static_cast<const uint8_t*>(kv) + static_cast<int64_t>(id) * kMlaFp8TokenBytes;
+    const uint8_t* src = valid ? static_cast<const uint8_t*>(kv) + static_cast<int64_t>(id) * kMlaFp8TokenBytes
+                               : static_cast<const uint8_t*>(safe);
     codes[0] = *reinterpret_cast<const u32x4*>(src + 16 * j);
     codes[1] = *reinterpret_cast<const u32x4*>(src + 256 + 16 * j);
     scales = *reinterpret_cast<const u32x4*>(src + 512);
-    if (j < 8) tail = *reinterpret_cast<const u32x4*>(src + 528 + 16 * j);
+    tail = *reinterpret_cast<const u32x4*>(src + 528 + 16 * (j & 7));
   }
 
   __device__ __forceinline__ void store(uint16_t* buf, uint8_t* vflag) const {
@@ -182,10 +190,23 @@ struct StagedFp8 {
   }
 };
 
-// Entry of this thread's row in the tile starting at t0 (-1 past the piece).
-__device__ __forceinline__ int32_t tile_entry(const int32_t* __restrict__ idx, int t0, int n) {
+// Entry of this thread's row in the tile starting at t0, as loaded (the load
+// is always issued, clamped into the piece; n >= 1), and whether that row
+// lies inside the piece. The two are combined only where the entry is used,
+// so nothing is computed from the loaded value next to its load (which would
+// make the wave wait for the load, and for every load before it, at once).
+struct Entry {
+  int32_t id;
+  bool in_piece;
+};
+__device__ __forceinline__ Entry tile_entry(const int32_t* __restrict__ idx, int t0, int n) {
   const int tok = t0 + static_cast<int>(threadIdx.x) / kThreadsPerRow;
-  return tok < n ? idx[tok] : -1;
+  return Entry{idx[min(tok, n - 1)], tok < n};
+}
+__device__ __forceinline__ int32_t entry_id(Entry e) {
+  int32_t id = e.id;
+  asm volatile("" : "+v"(id));
+  return e.in_piece ? id : -1;
 }
 
 struct State {
@@ -335,6 +356,9 @@ __global__ __launch_bounds__(kThreads) void mla_partial_kernel(
   // (partner's half scores, softmax, P.V) and computes its half scores of
   // tile t+1. Entries past the piece read as -1 (masked, nothing loaded).
   const int n_tiles = n > 0 ? (n + kTileTok - 1) / kTileTok : 0;
+  // An in-bounds row for the loads of masked entries: pool row 0, or this
+  // row's q (at least one 1152-byte row) when the pool is empty.
+  const void* safe = pool_tokens > 0 ? kv : static_cast<const void*>(q + static_cast<int64_t>(b) * num_qo_heads * kMlaDqk);
   Staged sa, sb;
   f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
   if (n_tiles > 0) {
@@ -346,16 +370,18 @@ __global__ __launch_bounds__(kThreads) void mla_partial_kernel(
       for (int i = threadIdx.x; i < 3 * kBufU16 / 8; i += kThreads)
         reinterpret_cast<u32x4*>(lds)[i] = zero;
     }
-    sa.load(tile_entry(idx, 0, n), pool_tokens, kv);
-    sb.load(tile_entry(idx, kTileTok, n), pool_tokens, kv);
+    sa.load(entry_id(tile_entry(idx, 0, n)), pool_tokens, kv, safe);
+    sb.load(entry_id(tile_entry(idx, kTileTok, n)), pool_tokens, kv, safe);
     __syncthreads();   // every wave's zeros land before any wave stores a row
-    int32_t id_a = tile_entry(idx, 2 * kTileTok, n);
-    int32_t id_b = tile_entry(idx, 3 * kTileTok, n);
+    Entry id_a = tile_entry(idx, 2 * kTileTok, n);
+    Entry id_b = tile_entry(idx, 3 * kTileTok, n);
+    // Loads leave in the loop's order (a set's rows, then the entry it loads
+    // next), so the loop starts with the same loads pending as every step.
     sa.store(lds, vflag[0]);
-    sa.load(id_a, pool_tokens, kv);                 // tile 2
-    sb.store(lds + kBufU16, vflag[1]);
-    sb.load(id_b, pool_tokens, kv);                 // tile 3
+    sa.load(entry_id(id_a), pool_tokens, kv, safe); // tile 2
     id_a = tile_entry(idx, 4 * kTileTok, n);
+    sb.store(lds + kBufU16, vflag[1]);
+    sb.load(entry_id(id_b), pool_tokens, kv, safe); // tile 3
     id_b = tile_entry(idx, 5 * kTileTok, n);
     __syncthreads();
     if (group_ok) {
@@ -365,33 +391,38 @@ __global__ __launch_bounds__(kThreads) void mla_partial_kernel(
     }
     __syncthreads();
     int cur = 0;                                    // buffer of tile t
-    for (int t = 0; t < n_tiles; t += 2) {
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        if (k == 1 && t + 1 >= n_tiles) break;
-        const int tt = t + k;
-        Staged& set = k == 0 ? sa : sb;
-        int32_t& id_set = k == 0 ? id_a : id_b;
-        const int nxt = cur == 2 ? 0 : cur + 1;     // buffer of tile tt+1
-        const int far = nxt == 2 ? 0 : nxt + 1;     // buffer of tile tt+2
-        set.store(lds + far * kBufU16, vflag[far]); // tile tt+2
-        set.load(id_set, pool_tokens, kv);          // tile tt+4
-        id_set = tile_entry(idx, (tt + 6) * kTileTok, n);
-        if (group_ok) {
-          const f32x4 f0 = s0 + xscore[tt & 1][partner][0][lane];
-          const f32x4 f1 = s1 + xscore[tt & 1][partner][1][lane];
-          // Scores of tile tt+1 first (in the last step they are computed from
-          // a buffer holding finite older data and never used): their MFMAs
-          // run while the softmax of tile tt is on the vector ALU.
-          half_scores(lds + nxt * kBufU16, qf, half, r, c, s0, s1);
-          softmax_pv(lds + cur * kBufU16, vflag[cur], f0, f1, scale_log2, half, r, c, st);
-          xscore[(tt + 1) & 1][w][0][lane] = s0;
-          xscore[(tt + 1) & 1][w][1][lane] = s1;
-        }
-        __syncthreads();
-        cur = nxt;
+    // Step tt: store tile tt+2 from `set`, reload `set` with tile tt+4, fetch
+    // the entry of tile tt+6, then finish tile tt and score tile tt+1.
+    auto step = [&](int tt, Staged& set, Entry& id_set) {
+      const int nxt = cur == 2 ? 0 : cur + 1;       // buffer of tile tt+1
+      const int far = nxt == 2 ? 0 : nxt + 1;       // buffer of tile tt+2
+      set.store(lds + far * kBufU16, vflag[far]);   // tile tt+2
+      set.load(entry_id(id_set), pool_tokens, kv, safe);   // tile tt+4
+      id_set = tile_entry(idx, (tt + 6) * kTileTok, n);
+      if (group_ok) {
+        const f32x4 f0 = s0 + xscore[tt & 1][partner][0][lane];
+        const f32x4 f1 = s1 + xscore[tt & 1][partner][1][lane];
+        // Scores of tile tt+1 first (in the last step they are computed from
+        // a buffer holding finite older data and never used): their MFMAs
+        // run while the softmax of tile tt is on the vector ALU.
+        half_scores(lds + nxt * kBufU16, qf, half, r, c, s0, s1);
+        softmax_pv(lds + cur * kBufU16, vflag[cur], f0, f1, scale_log2, half, r, c, st);
+        xscore[(tt + 1) & 1][w][0][lane] = s0;
+        xscore[(tt + 1) & 1][w][1][lane] = s1;
       }
+      __syncthreads();
+      cur = nxt;
+    };
+    // Whole pairs of steps in the loop and an odd last step after it, so the
+    // loop never leaves between the two steps of a pair (which would give the
+    // loop head a path with fewer loads in flight, and the compiler would
+    // then wait for every load at the top of each pair).
+    int t = 0;
+    for (; t + 1 < n_tiles; t += 2) {
+      step(t, sa, id_a);
+      step(t + 1, sb, id_b);
     }
+    if (t < n_tiles) step(t, sa, id_a);
   }
 
   float l_tot = st.l + __shfl_xor(st.l, 16);

@@ -28,6 +28,7 @@ struct pkv_plan {
   int64_t max_seq_pages;         // block-table plans: most pages any sequence needs
   pkv::Partition part;
   std::vector<int32_t> tables;   // worker offsets, segments, merge records, as uploaded
+  pkv::FirstSegments firsts;     // first segments' id positions, for the kernel arguments
   size_t off_wptr, off_segs, off_merges, off_part_o, off_part_lse, ws_bytes;
   void* workspace;               // device buffer the tables were uploaded to (or NULL)
 };
@@ -165,6 +166,16 @@ pkv_status make_plan(const int32_t* kv_indptr_host, int32_t batch, int32_t num_q
     t[4] = sb < se ? kv_indptr_host[sg.b] : 0; t[5] = sb; t[6] = se; t[7] = 0;
   }
   const size_t n_wrec = 8 * n_workers;
+  // The first segment of the first kFirstArgWorkers workers, for the kernel
+  // arguments (see kernels.h).
+  const int32_t n_firsts = static_cast<int32_t>(std::min<size_t>(n_workers, pkv::kFirstArgWorkers));
+  for (int32_t w = 0; w < n_firsts; ++w) {
+    const int32_t* r = p->tables.data() + 8 * static_cast<size_t>(w);
+    const bool has = r[5] < r[6];
+    p->firsts.v[3 * w] = has ? (block_table ? r[0] : r[4] + r[1]) : 0;
+    p->firsts.v[3 * w + 1] = has && block_table ? r[1] : 0;
+    p->firsts.v[3 * w + 2] = has ? r[2] - r[1] : 0;
+  }
   for (const auto& sg : pt.segments) {
     t[0] = sg.b; t[1] = sg.tok_begin; t[2] = sg.tok_end; t[3] = sg.slot;
     t[4] = kv_indptr_host[sg.b]; t[5] = 0; t[6] = 0; t[7] = 0;
@@ -305,7 +316,8 @@ pkv_status launch_run(const pkv_plan* plan, const void* q, const void* k_pool, c
   const float log2e = 1.4426950408889634f;
   hipError_t e = pkv::launch_decode_partial(
       reinterpret_cast<const int32_t*>(ws + plan->off_wptr),
-      reinterpret_cast<const int32_t*>(ws + plan->off_segs), plan->part.n_workers,
+      reinterpret_cast<const int32_t*>(ws + plan->off_segs), plan->firsts,
+      plan->part.n_workers,
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pool),
       static_cast<const uint16_t*>(v_pool), addr, sm_scale * log2e, static_cast<uint16_t*>(out),
       lse, reinterpret_cast<float*>(ws + plan->off_part_o),
@@ -521,6 +533,7 @@ pkv_status pkv_merge(const pkv_plan* plan, void* workspace, size_t workspace_byt
                 workspace_bytes, plan->ws_bytes);
   char* ws = static_cast<char*>(workspace);
   hipError_t e = pkv::launch_merge(reinterpret_cast<const int32_t*>(ws + plan->off_merges),
+                                   plan->tables.data() + plan->off_merges / sizeof(int32_t),
                                    static_cast<int32_t>(plan->part.merges.size()),
                                    reinterpret_cast<const float*>(ws + plan->off_part_o),
                                    reinterpret_cast<const float*>(ws + plan->off_part_lse),

@@ -199,23 +199,29 @@ struct TokenRows<true> {
   __device__ __forceinline__ int32_t operator()(int j) const { return row_of(fetch(j), j); }
 };
 
-// Decodes tokens [lo, lo + n) of sequence b (n > 0) with all four waves of the
-// workgroup and writes either the final out/lse (slot < 0) or a partial.
+// Decodes the n > 0 tokens of a segment of sequence b, whose pool rows `ids`
+// gives, with all four waves of the workgroup and writes either the final
+// out/lse (slot < 0) or a partial.
 template <bool kTable>
 __device__ __forceinline__ void process_segment(
-    int b, int lo, int n, int slot, int seq_offset, const uint16_t* __restrict__ q,
+    const TokenRows<kTable>& ids, int b, int n, int slot, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k_pool, const uint16_t* __restrict__ v_pool,
-    const KvAddressing& addr, float scale_log2, uint16_t* __restrict__ out,
-    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse,
-    uint16_t* lds) {
+    float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
+    float* __restrict__ part_o, float* __restrict__ part_lse, uint16_t* lds) {
   const int lane = threadIdx.x & 63;
   const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // KV head of this wave
   const int r = lane & 15;
   const int c = lane >> 4;
   const int head = g * kGroup + r;   // a real query head only for r < kGroup
-
-  const TokenRows<kTable> ids(addr, b, lo, seq_offset);
   const int last = n - 1;
+
+  // The ids of the first two tiles are fetched first: they depend only on
+  // the segment's position, so (for a worker's first segment, whose position
+  // comes with the kernel arguments) they leave before q, which needs b.
+  const int ja0 = min(r, last), ja1 = min(16 + r, last);
+  const int jn0 = min(kTileTok + r, last), jn1 = min(kTileTok + 16 + r, last);
+  int32_t a0 = ids.fetch(ja0), a1 = ids.fetch(ja1);
+  int32_t n0 = ids.fetch(jn0), n1 = ids.fetch(jn1);
 
   // Q as the B operand: lane (r, c) holds q[head r][32x + 8c, +8) for k-step x.
   u32x4 qf[4];
@@ -248,13 +254,9 @@ __device__ __forceinline__ void process_segment(
   const int n_rounds = n_tiles / kPipeTiles;
   static_assert(kPipeTiles == 2, "the prologue below fills a ring of two tiles");
   Tile ring[kPipeTiles];
-  // The ids of the first two tiles are fetched together, before any K/V load,
+  // The first two tiles' ids (fetched above) are all in before any K/V load,
   // so the loop starts with the second tile's rows known and no load pending
   // but the first tile's.
-  const int ja0 = min(r, last), ja1 = min(16 + r, last);
-  const int jn0 = min(kTileTok + r, last), jn1 = min(kTileTok + 16 + r, last);
-  int32_t a0 = ids.fetch(ja0), a1 = ids.fetch(ja1);
-  int32_t n0 = ids.fetch(jn0), n1 = ids.fetch(jn1);
   asm volatile("" : "+v"(a0), "+v"(a1), "+v"(n0), "+v"(n1));
   load_tile(ring[0], k_pool, v_pool, ids.row_of(a0, ja0), ids.row_of(a1, ja1), g, c);
   int32_t next0 = ids.row_of(n0, jn0);
@@ -317,25 +319,47 @@ __device__ __forceinline__ void process_segment(
   }
 }
 
-// One workgroup per worker: it walks its segments in order.
+// One workgroup per worker: it walks its segments in order. The first
+// kFirstArgWorkers workers find where their first segment's ids start in the
+// kernel arguments (CSR: (kv_indptr[b] + tok_begin, 0, n); block table: (b,
+// tok_begin, n); n = 0 if the worker has no segment), so its id loads leave
+// one memory round trip earlier than the worker's record, which still
+// supplies b, the slot and the segment range.
 template <bool kTable>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_partial_kernel(
     const int32_t* __restrict__ workers, const int32_t* __restrict__ segments,
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
-    const uint16_t* __restrict__ v_pool, KvAddressing addr, float scale_log2,
-    uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
-    float* __restrict__ part_lse) {
+    const FirstSegments firsts, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ k_pool, const uint16_t* __restrict__ v_pool, KvAddressing addr,
+    float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
+    float* __restrict__ part_o, float* __restrict__ part_lse) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[kHkv * kWaveLdsU16];
-  const int32_t* wrec = workers + 8 * blockIdx.x;   // first segment inline, then its range
+  const int w = blockIdx.x;
+  const bool first_in_args = w < kFirstArgWorkers;
+  // Read (clamped in range) before any branch, so the loads go out together
+  // with the other argument loads.
+  const int wf = min(w, kFirstArgWorkers - 1);
+  int f0 = firsts.v[3 * wf], f1 = firsts.v[3 * wf + 1], n = firsts.v[3 * wf + 2];
+  int wofs = 8 * w;
+  asm volatile("" : "+s"(f0), "+s"(f1), "+s"(n), "+s"(wofs));
+  const int32_t* wrec = workers + wofs;   // first segment inline, then its range
+  if (first_in_args) {
+    if (n > 0) {
+      const TokenRows<kTable> ids(addr, kTable ? f0 : 0, f1, kTable ? 0 : f0);
+      process_segment<kTable>(ids, wrec[0], n, wrec[3], q, k_pool, v_pool, scale_log2, out, lse,
+                              part_o, part_lse, lds);
+    }
+  }
   const int s_begin = wrec[5];
   const int s_end = wrec[6];
-  for (int s = s_begin; s < s_end; ++s) {
+  for (int s = first_in_args ? s_begin + 1 : s_begin; s < s_end; ++s) {
     const int32_t* seg = s == s_begin ? wrec : segments + 8 * s;
     const int lo = seg[1];
     const int n = seg[2] - lo;
-    if (n > 0)
-      process_segment<kTable>(seg[0], lo, n, seg[3], seg[4], q, k_pool, v_pool, addr, scale_log2,
-                              out, lse, part_o, part_lse, lds);
+    if (n > 0) {
+      const TokenRows<kTable> ids(addr, seg[0], lo, seg[4]);
+      process_segment<kTable>(ids, seg[0], n, seg[3], q, k_pool, v_pool, scale_log2, out, lse,
+                              part_o, part_lse, lds);
+    }
   }
 }
 
@@ -395,14 +419,31 @@ __device__ __forceinline__ void merge_round(const float* part_o, const float* pa
 // part_o and part_lse are not marked __restrict__: loads from restrict
 // read-only arguments may be re-issued next to their uses to save registers,
 // which would serialise the round's loads.
+// Merge records of up to kArgMerges split sequences travel in the kernel
+// arguments: a workgroup reads its record together with the other arguments
+// instead of one memory round trip later.
+constexpr int kArgMerges = 256;
+struct MergeRecords {
+  int32_t v[3 * kArgMerges];   // (b, first_slot, n_segments) per record
+};
+
+template <bool kInArgs>
 __global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ merges,
+                                                    const MergeRecords recs,
                                                     const float* part_o, const float* part_lse,
                                                     uint16_t* __restrict__ out,
                                                     float* __restrict__ lse) {
-  const int32_t* m = merges + 4 * blockIdx.x;
-  const int b = m[0];
-  const int first = m[1];
-  const int k = m[2];
+  int b, first, k;
+  if (kInArgs) {
+    b = recs.v[3 * blockIdx.x];
+    first = recs.v[3 * blockIdx.x + 1];
+    k = recs.v[3 * blockIdx.x + 2];
+  } else {
+    const int32_t* m = merges + 4 * blockIdx.x;
+    b = m[0];
+    first = m[1];
+    k = m[2];
+  }
   const int lane = threadIdx.x & 63;
   const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
   float top = kNegInf, den = 0.f;
@@ -440,28 +481,41 @@ __global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ 
 }  // namespace
 
 hipError_t launch_decode_partial(const int32_t* workers, const int32_t* segments,
-                                 int32_t n_workers, const uint16_t* q,
-                                 const uint16_t* k_pool, const uint16_t* v_pool,
-                                 const KvAddressing& addr, float sm_scale_log2, uint16_t* out,
-                                 float* lse, float* part_o, float* part_lse, hipStream_t stream) {
+                                 const FirstSegments& firsts, int32_t n_workers,
+                                 const uint16_t* q, const uint16_t* k_pool,
+                                 const uint16_t* v_pool, const KvAddressing& addr,
+                                 float sm_scale_log2, uint16_t* out, float* lse, float* part_o,
+                                 float* part_lse, hipStream_t stream) {
   if (n_workers <= 0) return hipSuccess;
   if (addr.kv_indptr == nullptr) {
     hipLaunchKernelGGL(decode_partial_kernel<true>, dim3(n_workers), dim3(kThreads), 0, stream,
-                       workers, segments, q, k_pool, v_pool, addr, sm_scale_log2, out, lse,
-                       part_o, part_lse);
+                       workers, segments, firsts, q, k_pool, v_pool, addr,
+                       sm_scale_log2, out, lse, part_o, part_lse);
   } else {
     hipLaunchKernelGGL(decode_partial_kernel<false>, dim3(n_workers), dim3(kThreads), 0, stream,
-                       workers, segments, q, k_pool, v_pool, addr, sm_scale_log2, out, lse,
-                       part_o, part_lse);
+                       workers, segments, firsts, q, k_pool, v_pool, addr,
+                       sm_scale_log2, out, lse, part_o, part_lse);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_merge(const int32_t* merges, int32_t n_merges, const float* part_o,
-                        const float* part_lse, uint16_t* out, float* lse, hipStream_t stream) {
+hipError_t launch_merge(const int32_t* merges, const int32_t* merges_host, int32_t n_merges,
+                        const float* part_o, const float* part_lse, uint16_t* out, float* lse,
+                        hipStream_t stream) {
   if (n_merges <= 0) return hipSuccess;
-  hipLaunchKernelGGL(merge_kernel, dim3(n_merges, kHq / 4), dim3(256), 0, stream, merges, part_o,
-                     part_lse, out, lse);
+  MergeRecords recs;
+  if (merges_host != nullptr && n_merges <= kArgMerges) {
+    for (int i = 0; i < n_merges; ++i) {
+      recs.v[3 * i] = merges_host[4 * i];
+      recs.v[3 * i + 1] = merges_host[4 * i + 1];
+      recs.v[3 * i + 2] = merges_host[4 * i + 2];
+    }
+    hipLaunchKernelGGL(merge_kernel<true>, dim3(n_merges, kHq / 4), dim3(256), 0, stream, merges,
+                       recs, part_o, part_lse, out, lse);
+  } else {
+    hipLaunchKernelGGL(merge_kernel<false>, dim3(n_merges, kHq / 4), dim3(256), 0, stream, merges,
+                       recs, part_o, part_lse, out, lse);
+  }
   return hipGetLastError();
 }
 

@@ -28,19 +28,32 @@ struct KvAddressing {
   int32_t page_shift;
 };
 
+// Where the first segment's ids start, for workers 0 .. kFirstArgWorkers - 1,
+// passed in the kernel arguments: CSR (kv_indptr[b] + tok_begin, 0, n), block
+// table (b, tok_begin, n), with n = tok_end - tok_begin (0 for a worker with
+// no segment). Entries past the launch's worker count are never read.
+constexpr int kFirstArgWorkers = 256;
+struct FirstSegments {
+  int32_t v[3 * kFirstArgWorkers];
+};
+
 // One workgroup per worker; worker w decodes the segments [s_begin, s_end)
 // named by its record workers[8w .. 8w+8) = (the first segment's five fields,
 // s_begin, s_end, 0); segment records are 8 int32:
 // (b, tok_begin, tok_end, slot, kv_indptr[b], 0, 0, 0).
 hipError_t launch_decode_partial(const int32_t* workers, const int32_t* segments,
-                                 int32_t n_workers, const uint16_t* q,
-                                 const uint16_t* k_pool, const uint16_t* v_pool,
-                                 const KvAddressing& addr, float sm_scale_log2, uint16_t* out,
-                                 float* lse, float* part_o, float* part_lse, hipStream_t stream);
+                                 const FirstSegments& firsts, int32_t n_workers,
+                                 const uint16_t* q, const uint16_t* k_pool,
+                                 const uint16_t* v_pool, const KvAddressing& addr,
+                                 float sm_scale_log2, uint16_t* out, float* lse, float* part_o,
+                                 float* part_lse, hipStream_t stream);
 
-// One workgroup per (merge record (b, first_slot, n_segments, 0), query head).
-hipError_t launch_merge(const int32_t* merges, int32_t n_merges, const float* part_o,
-                        const float* part_lse, uint16_t* out, float* lse, hipStream_t stream);
+// One workgroup per (merge record (b, first_slot, n_segments, 0), four query
+// heads). merges_host, a host copy of the records, lets up to 256 records
+// travel in the kernel arguments (NULL: the kernel reads `merges`).
+hipError_t launch_merge(const int32_t* merges, const int32_t* merges_host, int32_t n_merges,
+                        const float* part_o, const float* part_lse, uint16_t* out, float* lse,
+                        hipStream_t stream);
 
 }  // namespace pkv
 

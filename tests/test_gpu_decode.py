@@ -159,6 +159,9 @@ def test_sm_scale_argument():
     w0 = make_gqa(301, [50, 700], pool_pages=800, sm_scale=0.0)
     want0 = ref.gqa_paged_decode(w0.q, w0.k_pool, w0.v_pool, w0.kv_indptr, w0.kv_indices, 0.0)
     check(w0, want0, run_gpu(w0), "sm_scale=0")
+    wn = make_gqa(302, [50, 700], pool_pages=800, sm_scale=-1.0 / np.sqrt(128.0))
+    wantn = ref.gqa_paged_decode(wn.q, wn.k_pool, wn.v_pool, wn.kv_indptr, wn.kv_indices, wn.sm_scale)
+    check(wn, wantn, run_gpu(wn), "sm_scale<0")
 
 
 def test_explicit_stream():

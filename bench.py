@@ -371,7 +371,7 @@ def main():
     ap.add_argument("--no-split", action="store_true")
     ap.add_argument("--chunk", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=10.0)
-    ap.add_argument("--event-every", type=int, default=4,
+    ap.add_argument("--event-every", type=int, default=10,
                     help="bracket the decode kernel with HIP events on every n-th timed step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",

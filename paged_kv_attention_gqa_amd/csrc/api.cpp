@@ -28,7 +28,7 @@ struct pkv_plan {
   int64_t max_seq_pages;         // block-table plans: most pages any sequence needs
   pkv::Partition part;
   std::vector<int32_t> tables;   // worker offsets, segments, merge records, as uploaded
-  pkv::FirstSegments firsts;     // first segments' id positions, for the kernel arguments
+  pkv::FirstSegments firsts{};   // first segments' id positions, for the kernel arguments
   size_t off_wptr, off_segs, off_merges, off_part_o, off_part_lse, ws_bytes;
   void* workspace;               // device buffer the tables were uploaded to (or NULL)
 };

@@ -503,7 +503,7 @@ hipError_t launch_merge(const int32_t* merges, const int32_t* merges_host, int32
                         const float* part_o, const float* part_lse, uint16_t* out, float* lse,
                         hipStream_t stream) {
   if (n_merges <= 0) return hipSuccess;
-  MergeRecords recs;
+  MergeRecords recs{};
   if (merges_host != nullptr && n_merges <= kArgMerges) {
     for (int i = 0; i < n_merges; ++i) {
       recs.v[3 * i] = merges_host[4 * i];

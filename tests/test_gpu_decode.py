@@ -152,6 +152,23 @@ def test_unused_pages_never_read():
     check(w, oracle("tiny"), (out, lse), "tiny with NaN unused pages")
 
 
+def test_many_split_sequences_and_workers():
+    """Over 256 split sequences and over 256 workers: the merge records that do
+    not fit the kernel arguments are read from the workspace, and workers past
+    the first 256 take their first segment from their record."""
+    rng = np.random.default_rng(303)
+    lengths = [int(x) for x in rng.integers(65, 400, size=300)]
+    lengths[7] = 0
+    lengths[150] = 0
+    w = make_gqa(303, lengths)
+    plan = pkv.pkv_plan_create(w.kv_indptr, chunk_tokens=64)
+    flat = pkv.pkv_plan_export(plan)
+    assert flat[0] > 256 and flat[2] > 256                # workers, merge records
+    want = ref.gqa_paged_decode(w.q, w.k_pool, w.v_pool, w.kv_indptr, w.kv_indices, w.sm_scale)
+    check(w, want, run_gpu(w, chunk_tokens=64), "300 sequences, 64-token chunks")
+    check(w, want, run_gpu(w), "300 sequences, default plan")
+
+
 def test_sm_scale_argument():
     w = make_gqa(300, [50, 700], pool_pages=800, sm_scale=0.3)
     want = ref.gqa_paged_decode(w.q, w.k_pool, w.v_pool, w.kv_indptr, w.kv_indices, w.sm_scale)

@@ -29,6 +29,7 @@ struct pkv_plan {
   pkv::Partition part;
   std::vector<int32_t> tables;   // worker offsets, segments, merge records, as uploaded
   pkv::FirstSegments firsts{};   // first segments' id positions, for the kernel arguments
+  int32_t max_pieces = 0;        // most segments of one merge record
   size_t off_wptr, off_segs, off_merges, off_part_o, off_part_lse, ws_bytes;
   void* workspace;               // device buffer the tables were uploaded to (or NULL)
 };
@@ -181,7 +182,9 @@ pkv_status make_plan(const int32_t* kv_indptr_host, int32_t batch, int32_t num_q
     t[4] = kv_indptr_host[sg.b]; t[5] = 0; t[6] = 0; t[7] = 0;
     t += 8;
   }
+  p->max_pieces = 0;
   for (const auto& m : pt.merges) {
+    p->max_pieces = std::max(p->max_pieces, m.n_segments);
     t[0] = m.b; t[1] = m.first_slot; t[2] = m.n_segments; t[3] = m.pad;
     t += 4;
   }
@@ -535,6 +538,7 @@ pkv_status pkv_merge(const pkv_plan* plan, void* workspace, size_t workspace_byt
   hipError_t e = pkv::launch_merge(reinterpret_cast<const int32_t*>(ws + plan->off_merges),
                                    plan->tables.data() + plan->off_merges / sizeof(int32_t),
                                    static_cast<int32_t>(plan->part.merges.size()),
+                                   plan->max_pieces,
                                    reinterpret_cast<const float*>(ws + plan->off_part_o),
                                    reinterpret_cast<const float*>(ws + plan->off_part_lse),
                                    static_cast<uint16_t*>(out), lse, static_cast<hipStream_t>(stream));

@@ -427,8 +427,10 @@ struct MergeRecords {
   int32_t v[3 * kArgMerges];   // (b, first_slot, n_segments) per record
 };
 
+// One single-wave workgroup per (merge record, query head): a long record's
+// loads spread over as many CUs as it has heads.
 template <bool kInArgs>
-__global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ merges,
+__global__ __launch_bounds__(64) void merge_kernel(const int32_t* __restrict__ merges,
                                                     const MergeRecords recs,
                                                     const float* part_o, const float* part_lse,
                                                     uint16_t* __restrict__ out,
@@ -444,8 +446,8 @@ __global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ 
     first = m[1];
     k = m[2];
   }
-  const int lane = threadIdx.x & 63;
-  const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x;
+  const int h = blockIdx.y;
   float top = kNegInf, den = 0.f;
   f32x4 acc[2] = {};
   if (k <= 16) {
@@ -478,6 +480,79 @@ __global__ __launch_bounds__(256) void merge_kernel(const int32_t* __restrict__ 
   }
 }
 
+// Records of at most kSmallMerge pieces (the common case: a sequence cut a few
+// ways) take a cheaper shape: one single-wave workgroup per (record, four
+// heads); lane (hq, e) = (lane / 16, lane % 16) merges dims [8e, 8e + 8) of
+// head 4 blockIdx.y + hq over all pieces, so a wave needs nothing from other
+// lanes and the launch has a quarter of the waves of one per head (the
+// merge's time grows with the number of waves dispatched). All loads are
+// issued before any is used.
+constexpr int kSmallMerge = 8;
+
+template <bool kInArgs>
+__global__ __launch_bounds__(64) void merge_small_kernel(const int32_t* __restrict__ merges,
+                                                          const MergeRecords recs,
+                                                          const float* part_o,
+                                                          const float* part_lse,
+                                                          uint16_t* __restrict__ out,
+                                                          float* __restrict__ lse) {
+  int b, first, k;
+  if (kInArgs) {
+    b = recs.v[3 * blockIdx.x];
+    first = recs.v[3 * blockIdx.x + 1];
+    k = recs.v[3 * blockIdx.x + 2];
+  } else {
+    const int32_t* m = merges + 4 * blockIdx.x;
+    b = m[0];
+    first = m[1];
+    k = m[2];
+  }
+  const int lane = threadIdx.x;
+  const int h = 4 * blockIdx.y + (lane >> 4);
+  const int e = lane & 15;
+  float top = kNegInf, den = 0.f;
+  f32x4 acc[2] = {};
+  if (k > 0) {
+    float li[kSmallMerge];
+    f32x4 o[kSmallMerge][2];
+#pragma unroll
+    for (int j = 0; j < kSmallMerge; ++j) {
+      const int i = first + min(j, k - 1);   // past the end: the last piece again, weight 0
+      li[j] = part_lse[static_cast<int64_t>(i) * kHq + h];
+      const float* src = part_o + (static_cast<int64_t>(i) * kHq + h) * kHeadDim + 8 * e;
+      o[j][0] = *reinterpret_cast<const f32x4*>(src);
+      o[j][1] = *reinterpret_cast<const f32x4*>(src + 4);
+    }
+    // Every load above is issued before any of these statements (they
+    // clobber memory), and every use comes after its value passes one.
+#pragma unroll
+    for (int j = 0; j < kSmallMerge; ++j) asm volatile("" : "+v"(li[j]) :: "memory");
+#pragma unroll
+    for (int j = 0; j < kSmallMerge; ++j) asm volatile("" : "+v"(o[j][0]), "+v"(o[j][1]) :: "memory");
+#pragma unroll
+    for (int j = 0; j < kSmallMerge; ++j)
+      if (j < k) top = fmaxf(top, li[j]);
+    if (top != kNegInf) {
+#pragma unroll
+      for (int j = 0; j < kSmallMerge; ++j) {
+        const float wj = (j < k && li[j] != kNegInf) ? __builtin_amdgcn_exp2f(li[j] - top) : 0.f;
+        den += wj;
+        acc[0] += wj * o[j][0];
+        acc[1] += wj * o[j][1];
+      }
+    }
+  }
+  const float inv = den > 0.f ? 1.0f / den : 0.f;
+  const f32x4 a = acc[0] * inv;
+  const f32x4 c = acc[1] * inv;
+  const u32x4 wd = {static_cast<uint32_t>(bf16_bits(a[0])) | (static_cast<uint32_t>(bf16_bits(a[1])) << 16),
+                    static_cast<uint32_t>(bf16_bits(a[2])) | (static_cast<uint32_t>(bf16_bits(a[3])) << 16),
+                    static_cast<uint32_t>(bf16_bits(c[0])) | (static_cast<uint32_t>(bf16_bits(c[1])) << 16),
+                    static_cast<uint32_t>(bf16_bits(c[2])) | (static_cast<uint32_t>(bf16_bits(c[3])) << 16)};
+  *reinterpret_cast<u32x4*>(out + (static_cast<int64_t>(b) * kHq + h) * kHeadDim + 8 * e) = wd;
+  if (e == 0) lse[b * kHq + h] = den > 0.f ? top + __log2f(den) : kNegInf;
+}
+
 }  // namespace
 
 hipError_t launch_decode_partial(const int32_t* workers, const int32_t* segments,
@@ -500,21 +575,31 @@ hipError_t launch_decode_partial(const int32_t* workers, const int32_t* segments
 }
 
 hipError_t launch_merge(const int32_t* merges, const int32_t* merges_host, int32_t n_merges,
-                        const float* part_o, const float* part_lse, uint16_t* out, float* lse,
-                        hipStream_t stream) {
+                        int32_t max_pieces, const float* part_o, const float* part_lse,
+                        uint16_t* out, float* lse, hipStream_t stream) {
   if (n_merges <= 0) return hipSuccess;
   MergeRecords recs{};
-  if (merges_host != nullptr && n_merges <= kArgMerges) {
+  const bool in_args = merges_host != nullptr && n_merges <= kArgMerges;
+  if (in_args) {
     for (int i = 0; i < n_merges; ++i) {
       recs.v[3 * i] = merges_host[4 * i];
       recs.v[3 * i + 1] = merges_host[4 * i + 1];
       recs.v[3 * i + 2] = merges_host[4 * i + 2];
     }
-    hipLaunchKernelGGL(merge_kernel<true>, dim3(n_merges, kHq / 4), dim3(256), 0, stream, merges,
-                       recs, part_o, part_lse, out, lse);
+  }
+  if (max_pieces <= kSmallMerge) {
+    if (in_args)
+      hipLaunchKernelGGL(merge_small_kernel<true>, dim3(n_merges, kHq / 4), dim3(64), 0, stream,
+                         merges, recs, part_o, part_lse, out, lse);
+    else
+      hipLaunchKernelGGL(merge_small_kernel<false>, dim3(n_merges, kHq / 4), dim3(64), 0, stream,
+                         merges, recs, part_o, part_lse, out, lse);
+  } else if (in_args) {
+    hipLaunchKernelGGL(merge_kernel<true>, dim3(n_merges, kHq), dim3(64), 0, stream, merges, recs,
+                       part_o, part_lse, out, lse);
   } else {
-    hipLaunchKernelGGL(merge_kernel<false>, dim3(n_merges, kHq / 4), dim3(256), 0, stream, merges,
-                       recs, part_o, part_lse, out, lse);
+    hipLaunchKernelGGL(merge_kernel<false>, dim3(n_merges, kHq), dim3(64), 0, stream, merges, recs,
+                       part_o, part_lse, out, lse);
   }
   return hipGetLastError();
 }

@@ -48,12 +48,14 @@ hipError_t launch_decode_partial(const int32_t* workers, const int32_t* segments
                                  float sm_scale_log2, uint16_t* out, float* lse, float* part_o,
                                  float* part_lse, hipStream_t stream);
 
-// One workgroup per (merge record (b, first_slot, n_segments, 0), four query
-// heads). merges_host, a host copy of the records, lets up to 256 records
-// travel in the kernel arguments (NULL: the kernel reads `merges`).
+// Merges the split sequences' partials: one workgroup per (merge record
+// (b, first_slot, n_segments, 0), group of query heads). max_pieces is the
+// largest n_segments of the records (it picks the kernel's shape);
+// merges_host, a host copy of the records, lets up to 256 records travel in
+// the kernel arguments (NULL: the kernel reads `merges`).
 hipError_t launch_merge(const int32_t* merges, const int32_t* merges_host, int32_t n_merges,
-                        const float* part_o, const float* part_lse, uint16_t* out, float* lse,
-                        hipStream_t stream);
+                        int32_t max_pieces, const float* part_o, const float* part_lse,
+                        uint16_t* out, float* lse, hipStream_t stream);
 
 }  // namespace pkv
 

@@ -36,11 +36,13 @@
 //   out-of-range tokens of the last tile re-read the item's last page, which
 //   keeps every load unconditional, and get score -inf, i.e. weight exactly 0.
 // * Scores are scaled by sm_scale*log2(e) in fp32 and exponentiated with
-//   exp2; the running max is reduced across the 4 lane rows with shuffles,
-//   the running sum is kept per lane and reduced once at the end.
+//   exp2; the running max is reduced across the 4 lane rows with the
+//   cross-lane swaps v_permlane16_swap / v_permlane32_swap (vector ALU, no
+//   LDS), the running sum is kept per lane and reduced once at the end.
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
+#include "lanes.h"
 
 namespace pkv {
 namespace {
@@ -121,8 +123,7 @@ __device__ __forceinline__ void compute_tile(const Tile& t, int t0, int n, const
     p[4 + i] = (tok + 16 < n) ? s1[i] * scale_log2 : kNegInf;
     mx = fmaxf(mx, fmaxf(p[i], p[4 + i]));
   }
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = max_xor32(max_xor16(mx));
   const float m_new = fmaxf(st.m, mx);   // finite: every tile holds a valid token
   const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
   float psum = 0.f;
@@ -293,8 +294,7 @@ __device__ __forceinline__ void process_segment(
   for (int k = 0; k < kPipeTiles - 1; ++k)
     if (k < rest) compute_tile(ring[k], t0 + kTileTok * k, n, qf, scale_log2, r, c, lw, st);
 
-  float l_tot = st.l + __shfl_xor(st.l, 16);
-  l_tot += __shfl_xor(l_tot, 32);
+  const float l_tot = sum_xor32(sum_xor16(st.l));
   const float inv = 1.0f / l_tot;
   const float lse2 = st.m + __log2f(l_tot);
   if (r < kGroup) {

@@ -54,6 +54,7 @@
 
 #include <mutex>
 
+#include "lanes.h"
 #include "mla.h"
 
 namespace pkv {
@@ -253,8 +254,7 @@ __device__ __forceinline__ void softmax_pv(const uint16_t* buf, const uint8_t* v
     p[4 + j] = vflag[16 + 4 * c + j] ? s1[j] * scale_log2 : kNegInf;
     mx = fmaxf(mx, fmaxf(p[j], p[4 + j]));
   }
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = max_xor32(max_xor16(mx));
   // The reference max moves only when a head's max grows by more than
   // kRescaleSlack (log2 units), so the accumulators are rarely rescaled;
   // meanwhile p stays below 2^kRescaleSlack.
@@ -425,8 +425,7 @@ __global__ __launch_bounds__(kThreads) void mla_partial_kernel(
     if (t < n_tiles) step(t, sa, id_a);
   }
 
-  float l_tot = st.l + __shfl_xor(st.l, 16);
-  l_tot += __shfl_xor(l_tot, 32);
+  const float l_tot = sum_xor32(sum_xor16(st.l));
   const bool any = l_tot > 0.f;
   const float lse2 = any ? st.m + __log2f(l_tot) : kNegInf;
   if (!head_ok) return;

@@ -252,7 +252,10 @@ pkv_status pkv_append_kv(void* k_pool, void* v_pool, int64_t num_pages, int32_t 
  * indices int32 [batch, topk]; out bf16 [batch, num_qo_heads, d_v];
  * lse fp32 [batch, num_qo_heads]. Compiled for d_qk = 576, d_v = 512 and
  * num_qo_heads a multiple of 16 up to 128. workspace: device scratch of
- * pkv_gather_mla_workspace_size bytes.
+ * pkv_gather_mla_workspace_size bytes. Degenerate shapes are valid: with
+ * topk = 0 (indices may then be NULL) or pool_tokens = 0 (kv_pool may then
+ * be NULL) every row has no valid entry and gets out 0, lse -inf; batch = 0
+ * enqueues nothing.
  */
 pkv_status pkv_gather_mla_workspace_size(int32_t batch, int32_t num_qo_heads, int32_t d_qk,
                                          int32_t d_v, int32_t topk, size_t* bytes);

@@ -345,8 +345,9 @@ pkv_status gather_common(const void* q, const void* kv_pool, bool fp8_pool, int6
   if (pool_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "pool_tokens must be >= 0");
   if (!std::isfinite(sm_scale)) return fail(PKV_ERR_INVALID_ARG, "sm_scale must be finite");
   if (batch == 0) return ok();
-  if (q == nullptr || indices == nullptr || out == nullptr || lse == nullptr)
-    return fail(PKV_ERR_INVALID_ARG, "q, indices, out and lse must be non-NULL");
+  if (q == nullptr || out == nullptr || lse == nullptr)
+    return fail(PKV_ERR_INVALID_ARG, "q, out and lse must be non-NULL");
+  if (topk > 0 && indices == nullptr) return fail(PKV_ERR_INVALID_ARG, "indices is NULL");
   if (pool_tokens > 0 && kv_pool == nullptr) return fail(PKV_ERR_INVALID_ARG, "kv_pool is NULL");
   if (!aligned16(q) || !aligned16(kv_pool) || !aligned16(out) || !aligned16(workspace))
     return fail(PKV_ERR_INVALID_ARG, "q, kv_pool, out and workspace must be 16-byte aligned");

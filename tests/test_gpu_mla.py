@@ -83,6 +83,26 @@ def test_mla_scale_and_rerun():
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
+def test_mla_degenerate_shapes():
+    """Empty lists, an empty pool and an empty batch: every row has no valid
+    entry, so out is 0 and lse is -inf, as in the oracle."""
+    w = make_mla(54, batch=2, num_qo_heads=64, pool_tokens=100, topk=8)
+    empty = np.zeros((2, 0), np.int32)
+    got = run_gpu(w, indices=empty)
+    check(w, got, indices=empty, what="topk 0")
+    assert not got[0].any() and np.all(got[1] == -np.inf)
+    # pool of no rows: every id is out of range, so masked
+    out, lse = pkv.gather_mla(to_dev(w.q), torch.empty((0, 576), dtype=torch.bfloat16, device="cuda"),
+                              to_dev(w.indices), w.sm_scale, d_v=512)
+    torch.cuda.synchronize()
+    assert not bf16_to_np(out).any() and torch.all(lse == -torch.inf)
+    # no rows at all
+    out, lse = pkv.gather_mla(to_dev(w.q)[:0], to_dev(w.kv_pool), to_dev(w.indices)[:0],
+                              w.sm_scale, d_v=512)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 64, 512) and lse.shape == (0, 64)
+
+
 def test_mla_shape_errors():
     w = make_mla(53, batch=1, num_qo_heads=16, pool_tokens=100, topk=8)
     q = to_dev(w.q)

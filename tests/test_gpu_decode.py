@@ -73,6 +73,14 @@ def test_ragged_small(lengths, chunk):
     check(w, want, run_gpu(w, chunk_tokens=chunk), f"ragged {lengths} chunk={chunk}")
 
 
+def test_empty_batch():
+    """B = 0: nothing to decode; the call returns empty outputs."""
+    w = make_gqa(500, [], pool_pages=5)
+    for chunk in (0, 32):
+        out, lse = run_gpu(w, chunk_tokens=chunk)
+        assert out.shape == (0, 32, 128) and lse.shape == (0, 32)
+
+
 def test_many_short_sequences_per_worker():
     """3,000 sequences of 0-4 tokens and one of 5,000: the cost-balanced plan
     packs about ten short segments into a worker, and the long sequence is

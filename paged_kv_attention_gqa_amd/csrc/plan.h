@@ -4,10 +4,11 @@
 // to workers (one workgroup of the decode kernel each) so that every worker
 // gets about the same cost: a piece of n tokens costs its whole 32-token
 // tiles plus kSegmentCost tokens for starting a segment (measured: a
-// workgroup spends about one tile's time on each extra segment). Workers are
-// filled greedily under a cost budget, the smallest budget that needs at most
-// the allowed number of workers (found by bisection); cuts inside a sequence
-// fall on whole tiles. A worker's share is a list of segments
+// workgroup spends about half to one tile's time on each extra segment, and a
+// ragged last tile nearly a whole tile's). Workers are filled greedily under a
+// cost budget, the smallest budget that needs at most the allowed number of
+// workers (a galloping search, then bisection); cuts inside a sequence fall on
+// whole tiles. A worker's share is a list of segments
 // (b, tok_begin, tok_end, slot), one per sequence it touches, with token
 // positions relative to the sequence. A
 // sequence that lies inside one worker is written directly (slot = -1); a

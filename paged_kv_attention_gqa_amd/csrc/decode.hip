@@ -225,14 +225,16 @@ __device__ __forceinline__ void process_segment(
   int32_t n0 = ids.fetch(jn0), n1 = ids.fetch(jn1);
 
   // Q as the B operand: lane (r, c) holds q[head r][32x + 8c, +8) for k-step x.
+  // The 8 padding columns (r >= kGroup) repeat heads r - kGroup: their scores
+  // and outputs are computed and never stored, and every lane loads, so the
+  // compiler can count the loads in flight (a masked load made it wait for q
+  // before the first K/V loads).
   u32x4 qf[4];
-  if (r < kGroup) {
-    const uint16_t* qh = q + (static_cast<int64_t>(b) * kHq + head) * kHeadDim + 8 * c;
+  {
+    const uint16_t* qh =
+        q + (static_cast<int64_t>(b) * kHq + g * kGroup + (r & (kGroup - 1))) * kHeadDim + 8 * c;
 #pragma unroll
     for (int x = 0; x < 4; ++x) qf[x] = *reinterpret_cast<const u32x4*>(qh + 32 * x);
-  } else {
-#pragma unroll
-    for (int x = 0; x < 4; ++x) qf[x] = u32x4{0u, 0u, 0u, 0u};
   }
 
   Softmax st;

@@ -369,6 +369,8 @@ def main():
                     choices=sorted(WORKLOAD_TEXT) + ["mla", "mla_fp8", "append"])
     ap.add_argument("--replicas", type=int, default=0, help="pool copies to rotate (0 = auto)")
     ap.add_argument("--no-split", action="store_true")
+    ap.add_argument("--engine", default="mfma", choices=["mfma", "dot2"],
+                    help="units of the decode contractions: matrix cores or vector-ALU dot2")
     ap.add_argument("--chunk", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--event-every", type=int, default=10,
@@ -430,6 +432,7 @@ def main():
                                    workspace=ws)
         runs = [pkv.prepare_run(plan, q, k, v, indptr, indices, w.sm_scale, ws, out, lse)
                 for k, v in pools]
+    pkv.pkv_plan_set_engine(plan, args.engine)
     flat = pkv.pkv_plan_export(plan)
     torch.cuda.synchronize()
     merge = pkv.prepare_merge(plan, ws, out, lse)
@@ -471,7 +474,8 @@ def main():
     value = kv_bytes / (wall / args.steps) / 1e9
     alg = algorithmic_decode_bytes(w, flat)
     achieved = alg / decode_s / 1e9
-    traffic = read_traffic(args.config)
+    # The committed counter summaries were taken with the matrix-core engine.
+    traffic = read_traffic(args.config) if args.engine == "mfma" else None
 
     rec = {
         "metric": METRIC,
@@ -493,7 +497,8 @@ def main():
         "config": {"workload": WORKLOAD_TEXT[args.config], "name": args.config,
                    "batch": w.batch, "total_tokens": w.total_tokens,
                    "page_size": w.page_size,
-                   "split": not args.no_split, "workers": flat[0], "segments": flat[1],
+                   "split": not args.no_split, "engine": args.engine,
+                   "workers": flat[0], "segments": flat[1],
                    "merge_records": flat[2], "partial_slots": flat[3], "pool_replicas": reps,
                    "plan_host_us": round(plan_us, 1)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,

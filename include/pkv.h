@@ -119,6 +119,20 @@ pkv_status pkv_plan_workspace_size(const pkv_plan* plan, size_t* bytes);
 pkv_status pkv_plan_upload(pkv_plan* plan, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Which units run the decode kernel's two contractions (the scaled q.k scores
+ * and the P.V product of the GQA page's decode steps) for later pkv_run /
+ * pkv_block_table_run calls with this plan. PKV_ENGINE_MFMA (the default):
+ * the matrix cores, with the 8 query heads of a KV head padded to 16 MFMA
+ * columns. PKV_ENGINE_DOT2: the vector ALU, two bf16 products per lane and
+ * instruction into fp32 (v_dot2c_f32_bf16). Both compute the same
+ * definition with fp32 accumulation and P rounded to bf16; their results
+ * differ only by rounding order. Any other value returns PKV_ERR_INVALID_ARG
+ * and leaves the plan unchanged. Host only; the plan's tables do not change.
+ */
+enum { PKV_ENGINE_MFMA = 0, PKV_ENGINE_DOT2 = 1 };
+pkv_status pkv_plan_set_engine(pkv_plan* plan, int32_t engine);
+
+/*
  * Copy the plan's integer tables to host memory:
  * [n_workers, n_segments, n_merges, n_slots], then n_workers + 1 offsets of
  * each worker's first segment, then n_segments records

@@ -20,7 +20,8 @@ from ._build import LIB_PATH
 __all__ = [
     "PkvError", "Plan", "decode", "gather_mla", "library_path",
     "pkv_workspace_size", "pkv_plan_create", "pkv_plan_destroy", "pkv_plan_export",
-    "pkv_plan_workspace_size", "pkv_plan_upload",
+    "pkv_plan_workspace_size", "pkv_plan_upload", "pkv_plan_set_engine",
+    "PKV_ENGINE_MFMA", "PKV_ENGINE_DOT2",
     "pkv_run", "pkv_merge", "pkv_gather_mla_workspace_size", "pkv_gather_mla",
     "prepare_run", "prepare_merge", "prepare_gather_mla", "prepare_append_kv",
     "pkv_block_table_workspace_size", "pkv_block_table_plan_create", "pkv_block_table_run",
@@ -35,6 +36,10 @@ PKV_ERR_UNSUPPORTED = 2
 PKV_ERR_WORKSPACE_TOO_SMALL = 3
 PKV_ERR_PLAN_MISMATCH = 4
 PKV_ERR_HIP = 5
+
+PKV_ENGINE_MFMA = 0
+PKV_ENGINE_DOT2 = 1
+ENGINES = {"mfma": PKV_ENGINE_MFMA, "dot2": PKV_ENGINE_DOT2}
 
 # Every symbol include/pkv.h declares, with (restype, argtypes).
 _c = ctypes
@@ -51,6 +56,7 @@ SIGNATURES = {
     "pkv_plan_destroy": (None, [_P]),
     "pkv_plan_workspace_size": (_I32, [_P, _c.POINTER(_SZ)]),
     "pkv_plan_upload": (_I32, [_P, _P, _SZ, _P]),
+    "pkv_plan_set_engine": (_I32, [_P, _I32]),
     "pkv_plan_export": (_I32, [_P, _I32P, _SZ, _c.POINTER(_SZ)]),
     "pkv_run": (_I32, [_P, _P, _I32, _I32, _I32, _P, _P, _I64, _I32, _I32, _I32, _P, _I64, _P,
                        _I64, _c.c_float, _P, _SZ, _P, _P, _P]),
@@ -498,6 +504,13 @@ def pkv_plan_workspace_size(plan: Plan) -> int:
     return int(out.value)
 
 
+def pkv_plan_set_engine(plan: Plan, engine) -> None:
+    """Pick the decode contraction engine for this plan's runs: ``"mfma"``
+    (the default) or ``"dot2"``, or the integer PKV_ENGINE_* code."""
+    code = ENGINES[engine] if isinstance(engine, str) else int(engine)
+    _check(lib().pkv_plan_set_engine(plan.handle, code), "pkv_plan_set_engine")
+
+
 def pkv_plan_upload(plan: Plan, workspace, stream=None) -> None:
     _require(workspace, "workspace", (__import__("torch").uint8,))
     _check(lib().pkv_plan_upload(plan.handle, _ptr(workspace), workspace.numel(), _stream(stream)),
@@ -505,11 +518,13 @@ def pkv_plan_upload(plan: Plan, workspace, stream=None) -> None:
 
 
 def decode(q, k_pool, v_pool, kv_indptr, kv_indices, sm_scale: Optional[float] = None,
-           kv_indptr_host=None, allow_split=True, chunk_tokens=0, num_cus=0, stream=None):
+           kv_indptr_host=None, allow_split=True, chunk_tokens=0, num_cus=0, stream=None,
+           engine="mfma"):
     """Plan, run and merge one paged GQA decode; returns ``(out, lse)`` (bf16, fp32 base 2).
 
     ``sm_scale`` defaults to 1/sqrt(head_dim). ``kv_indptr_host`` (a host copy
-    of ``kv_indptr``) avoids a device-to-host copy when given.
+    of ``kv_indptr``) avoids a device-to-host copy when given. ``engine``
+    picks the contraction units (``"mfma"`` or ``"dot2"``).
     """
     import torch
     if sm_scale is None:
@@ -518,6 +533,7 @@ def decode(q, k_pool, v_pool, kv_indptr, kv_indices, sm_scale: Optional[float] =
         kv_indptr_host = kv_indptr.cpu()
     plan = pkv_plan_create(kv_indptr_host, q.shape[1], k_pool.shape[2], q.shape[2],
                            k_pool.shape[1], num_cus, allow_split, chunk_tokens)
+    pkv_plan_set_engine(plan, engine)
     ws = torch.empty(max(pkv_plan_workspace_size(plan), 16), dtype=torch.uint8, device=q.device)
     pkv_plan_upload(plan, ws, stream)
     out = torch.empty_like(q)
@@ -529,7 +545,7 @@ def decode(q, k_pool, v_pool, kv_indptr, kv_indices, sm_scale: Optional[float] =
 
 def decode_block_table(q, k_pool, v_pool, block_table, seq_lens_host,
                        sm_scale: Optional[float] = None, allow_split=True, chunk_tokens=0,
-                       num_cus=0, stream=None):
+                       num_cus=0, stream=None, engine="mfma"):
     """Plan, run and merge one paged GQA decode through a block table.
 
     ``k_pool``/``v_pool`` are ``[pages, page_size, Hkv, D]``; ``block_table``
@@ -541,6 +557,7 @@ def decode_block_table(q, k_pool, v_pool, block_table, seq_lens_host,
         sm_scale = 1.0 / math.sqrt(q.shape[-1])
     plan = pkv_block_table_plan_create(seq_lens_host, q.shape[1], k_pool.shape[2], q.shape[2],
                                        k_pool.shape[1], num_cus, allow_split, chunk_tokens)
+    pkv_plan_set_engine(plan, engine)
     ws = torch.empty(max(pkv_plan_workspace_size(plan), 16), dtype=torch.uint8, device=q.device)
     pkv_plan_upload(plan, ws, stream)
     out = torch.empty_like(q)

@@ -30,6 +30,7 @@ struct pkv_plan {
   std::vector<int32_t> tables;   // worker offsets, segments, merge records, as uploaded
   pkv::FirstSegments firsts{};   // first segments' id positions, for the kernel arguments
   int32_t max_pieces = 0;        // most segments of one merge record
+  pkv::DecodeEngine engine = pkv::DecodeEngine::kMfma;   // units of the decode contractions
   size_t off_wptr, off_segs, off_merges, off_part_o, off_part_lse, ws_bytes;
   void* workspace;               // device buffer the tables were uploaded to (or NULL)
 };
@@ -324,7 +325,8 @@ pkv_status launch_run(const pkv_plan* plan, const void* q, const void* k_pool, c
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pool),
       static_cast<const uint16_t*>(v_pool), addr, sm_scale * log2e, static_cast<uint16_t*>(out),
       lse, reinterpret_cast<float*>(ws + plan->off_part_o),
-      reinterpret_cast<float*>(ws + plan->off_part_lse), static_cast<hipStream_t>(stream));
+      reinterpret_cast<float*>(ws + plan->off_part_lse), plan->engine,
+      static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -451,6 +453,15 @@ pkv_status pkv_plan_upload(pkv_plan* plan, void* workspace, size_t workspace_byt
   if (plan == nullptr) return fail(PKV_ERR_INVALID_ARG, "plan is NULL");
   const pkv_status s = upload_plan(plan, workspace, workspace_bytes, stream);
   return s == PKV_OK ? ok() : s;
+}
+
+pkv_status pkv_plan_set_engine(pkv_plan* plan, int32_t engine) {
+  if (plan == nullptr) return fail(PKV_ERR_INVALID_ARG, "plan is NULL");
+  if (engine != PKV_ENGINE_MFMA && engine != PKV_ENGINE_DOT2)
+    return fail(PKV_ERR_INVALID_ARG, "engine must be PKV_ENGINE_MFMA (0) or PKV_ENGINE_DOT2 (1), got %d",
+                engine);
+  plan->engine = static_cast<pkv::DecodeEngine>(engine);
+  return ok();
 }
 
 pkv_status pkv_plan_export(const pkv_plan* plan, int32_t* dst, size_t n_int32, size_t* needed) {

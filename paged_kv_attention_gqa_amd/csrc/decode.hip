@@ -52,11 +52,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kGroup = kHq / kHkv;      // query heads per KV head
 constexpr int kTileTok = 32;            // tokens per wave per step
 constexpr int kRowU16 = kHeadDim + 16;  // LDS row of one token's V: 256 B + 32 B pad
-constexpr int kWaveLdsU16 = kTileTok * kRowU16;
 constexpr int kThreads = 64 * kHkv;
 constexpr int kPipeTiles = 2;           // register tile buffers per wave
 constexpr float kNegInf = -__builtin_huge_valf();
@@ -102,10 +102,12 @@ __device__ __forceinline__ void lds_wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__device__ __forceinline__ void compute_tile(const Tile& t, int t0, int n, const u32x4 (&qf)[4],
-                                             float scale_log2, int r, int c, uint16_t* lw,
-                                             Softmax& st) {
-  // Scores of the 32 tokens against the (padded) 16 heads.
+// First half of a tile: scores of the 32 tokens against the (padded) 16
+// heads, the online-softmax update, and the tile's V rows into LDS. After it
+// the tile's registers are free; pb holds P for compute_back.
+__device__ __forceinline__ void compute_front(const Tile& t, int t0, int n, const u32x4 (&qf)[4],
+                                              float scale_log2, int r, int c, uint16_t* lw,
+                                              Softmax& st, bf16x8& pb) {
   f32x4 s0 = {0.f, 0.f, 0.f, 0.f};
   f32x4 s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -148,10 +150,13 @@ __device__ __forceinline__ void compute_tile(const Tile& t, int t0, int n, const
   }
   lds_wave_sync();
 
-  bf16x8 pb;
 #pragma unroll
   for (int j = 0; j < 8; ++j) pb[j] = static_cast<__bf16>(p[j]);
+}
 
+// Second half: O^T += V^T P^T from the LDS copy of the tile's V rows.
+__device__ __forceinline__ void compute_back(const bf16x8& pb, int r, int c, const uint16_t* lw,
+                                             Softmax& st) {
   // A operand of block db: V[token 16*(j/4) + 4c + j%4][16*db + r], j = 0..7,
   // read with the transposing LDS load: within each 16-lane group it gives
   // lane i element i%4 of the 8-byte chunks addressed by lanes 4j + i/4, so
@@ -169,6 +174,324 @@ __device__ __forceinline__ void compute_tile(const Tile& t, int t0, int n, const
     st.acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), pb, st.acc[db], 0, 0, 0);
   }
 }
+
+// The two contraction engines a segment can run on. Each keeps the wave's
+// query heads and softmax state, consumes tiles as the pipeline in
+// process_segment delivers them, and writes the segment's result.
+//
+// Each tile is taken in two calls: front() (scores, softmax, V rows into LDS)
+// after which the tile's registers may be reloaded, and back() (P.V from
+// LDS).
+//
+// MfmaEngine: both contractions on v_mfma_f32_16x16x32_bf16 (compute_front,
+// compute_back).
+struct MfmaEngine {
+  static constexpr int kWaveLdsU16 = kTileTok * kRowU16;   // the V tile
+  static constexpr int kWavesPerEu = 2;
+  static constexpr bool kEarlyLoads = false;
+  u32x4 qf[4];
+  Softmax st;
+  bf16x8 pb;   // P of the tile between front() and back()
+
+  // Q as the B operand: lane (r, c) holds q[head r][32x + 8c, +8) for k-step
+  // x. The 8 padding columns (r >= kGroup) repeat heads r - kGroup: their
+  // scores and outputs are computed and never stored.
+  __device__ __forceinline__ void begin(const uint16_t* __restrict__ q, int b, int g, int r, int c) {
+    const uint16_t* qh =
+        q + (static_cast<int64_t>(b) * kHq + g * kGroup + (r & (kGroup - 1))) * kHeadDim + 8 * c;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) qf[x] = *reinterpret_cast<const u32x4*>(qh + 32 * x);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) st.acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st.m = kNegInf;
+    st.l = 0.f;
+  }
+
+  __device__ __forceinline__ void front(const Tile& t, int t0, int n, float scale_log2, int r,
+                                        int c, uint16_t* lw) {
+    compute_front(t, t0, n, qf, scale_log2, r, c, lw, st, pb);
+  }
+
+  __device__ __forceinline__ void back(int r, int c, const uint16_t* lw) {
+    compute_back(pb, r, c, lw, st);
+  }
+
+  __device__ __forceinline__ void finish(int b, int g, int slot, int r, int c,
+                                         uint16_t* __restrict__ out, float* __restrict__ lse,
+                                         float* __restrict__ part_o, float* __restrict__ part_lse) {
+    const int head = g * kGroup + r;   // a real query head only for r < kGroup
+    const float l_tot = sum_xor32(sum_xor16(st.l));
+    const float inv = 1.0f / l_tot;
+    const float lse2 = st.m + __log2f(l_tot);
+    if (r < kGroup) {
+      if (slot < 0) {
+        uint16_t* o = out + (static_cast<int64_t>(b) * kHq + head) * kHeadDim + 4 * c;
+  #pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          const f32x4 v = st.acc[db] * inv;
+          const u32x2 w = {static_cast<uint32_t>(bf16_bits(v[0])) |
+                               (static_cast<uint32_t>(bf16_bits(v[1])) << 16),
+                           static_cast<uint32_t>(bf16_bits(v[2])) |
+                               (static_cast<uint32_t>(bf16_bits(v[3])) << 16)};
+          *reinterpret_cast<u32x2*>(o + 16 * db) = w;
+        }
+        if (c == 0) lse[b * kHq + head] = lse2;
+      } else {
+        float* o = part_o + (static_cast<int64_t>(slot) * kHq + head) * kHeadDim + 4 * c;
+  #pragma unroll
+        for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(o + 16 * db) = st.acc[db] * inv;
+        if (c == 0) part_lse[static_cast<int64_t>(slot) * kHq + head] = lse2;
+      }
+    }
+  }
+};
+
+// Dot2Engine: both contractions on the vector ALU with v_dot2c_f32_bf16 (two
+// bf16 products summed into an fp32 accumulator per lane and instruction),
+// over the same tiles and the same K/V register layout as the MFMA engine.
+// * Scores: lane (r, c) holds dims {32x + 8c .. +8 | x < 4} of tokens r and
+//   16 + r, and forms their partial dot products with all 8 heads (q is read
+//   from the wave's LDS copy, 16 lanes sharing each 16-byte read). The four
+//   lanes of a token (c = 0..3) then sum their partials in two halving steps
+//   (split_sum_xor32, split_sum_xor16), after which lane (r, c) holds the full
+//   scores of tokens r and 16 + r for heads 2c and 2c + 1.
+// * Softmax: the tile max of a head is reduced over the 16 lanes of its row
+//   (DPP), and the 8 heads' maxima are shared with every lane by cross-lane
+//   swaps, so every lane can rescale its accumulators of all 8 heads; the
+//   running sum is kept per lane and reduced at the end of the segment.
+// * P.V: P (bf16) goes to LDS as [token quad][head][4 tokens]; lane (r, c)
+//   owns output dims 16c + r and 64 + 16c + r of all 8 heads and reads V^T
+//   pairs (two consecutive tokens of one dim) with ds_read_b64_tr_b16, each
+//   a dot2 operand against the matching pair of P, which all lanes read at the
+//   same LDS address.
+struct Dot2Engine {
+  static constexpr int kQU16 = kGroup * kHeadDim;   // the wave's q block, row-major by head
+  static constexpr int kPU16 = kTileTok * kGroup;   // P of one tile
+  static constexpr int kWaveLdsU16 = kTileTok * kRowU16 + kQU16 + kPU16;
+  static constexpr int kWavesPerEu = 2;
+  static constexpr bool kEarlyLoads = true;
+  u32x4 qa, qb;          // bytes [32 lane, +32) of the q block, until they go to LDS
+  float acc[kGroup][2];  // O[head h][dim 16c + r], O[head h][dim 64 + 16c + r]
+  float m_all[kGroup];   // running max of each head (the same in every lane)
+  float m_own[2];        // running max of heads 2c, 2c + 1 (equal to m_all's)
+  float l_own[2];        // this lane's share of their exp-sums
+
+  __device__ __forceinline__ void begin(const uint16_t* __restrict__ q, int b, int g, int r, int c) {
+    const int lane = 16 * c + r;
+    const uint16_t* qg = q + (static_cast<int64_t>(b) * kHq + g * kGroup) * kHeadDim + 16 * lane;
+    qa = *reinterpret_cast<const u32x4*>(qg);
+    qb = *reinterpret_cast<const u32x4*>(qg + 8);
+#pragma unroll
+    for (int h = 0; h < kGroup; ++h) {
+      acc[h][0] = 0.f;
+      acc[h][1] = 0.f;
+      m_all[h] = kNegInf;
+    }
+    m_own[0] = m_own[1] = kNegInf;
+    l_own[0] = l_own[1] = 0.f;
+  }
+
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                           __builtin_bit_cast(bf16x2, b), acc, false);
+  }
+
+  // The 8 heads' values of a per-row quantity (v[j] of row c belongs to head
+  // 2c + j) in every lane: out[2c' + j] = row c' value j.
+  static __device__ __forceinline__ void share_rows(const float (&v)[2], float (&out)[kGroup]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const lane_u32x2 p16 = pair_xor16(v[j]);   // rows c & ~1, c | 1
+      const unsigned lo = p16[0], hi = p16[1];
+      const lane_u32x2 a = pair_xor32(__builtin_bit_cast(float, lo));   // rows 0, 2
+      const lane_u32x2 e = pair_xor32(__builtin_bit_cast(float, hi));   // rows 1, 3
+      const unsigned a0 = a[0], a1 = a[1], e0 = e[0], e1 = e[1];
+      out[0 + j] = __builtin_bit_cast(float, a0);
+      out[2 + j] = __builtin_bit_cast(float, e0);
+      out[4 + j] = __builtin_bit_cast(float, a1);
+      out[6 + j] = __builtin_bit_cast(float, e1);
+    }
+  }
+
+  __device__ __forceinline__ void front(const Tile& t, int t0, int n, float scale_log2, int r,
+                                        int c, uint16_t* lw) {
+    uint16_t* lq = lw + kTileTok * kRowU16;
+    uint16_t* lp = lq + kQU16;
+    if (t0 == 0) {   // the segment's first tile: q to LDS
+      lds_wave_sync();
+      *reinterpret_cast<u32x4*>(lq + 16 * (16 * c + r)) = qa;
+      *reinterpret_cast<u32x4*>(lq + 16 * (16 * c + r) + 8) = qb;
+    }
+    lds_wave_sync();
+
+    // Partial scores of tokens r (mb 0) and 16 + r (mb 1) over this lane's
+    // dims, one 8-dim slice at a time: the slice's q reads (one per head)
+    // all leave before any is used, so a slice costs one LDS round trip.
+    float s[2][kGroup];
+#pragma unroll
+    for (int h = 0; h < kGroup; ++h) s[0][h] = s[1][h] = 0.f;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      __builtin_amdgcn_sched_barrier(0);
+      u32x4 qv[kGroup];
+#pragma unroll
+      for (int h = 0; h < kGroup; ++h)
+        qv[h] = *reinterpret_cast<const u32x4*>(lq + h * kHeadDim + 32 * x + 8 * c);
+#pragma unroll
+      for (int h = 0; h < kGroup; ++h) asm volatile("" : "+v"(qv[h]));
+#pragma unroll
+      for (int h = 0; h < kGroup; ++h) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t qe = qv[h][e];
+          const uint32_t k0 = t.k[0][x][e], k1 = t.k[1][x][e];
+          s[0][h] = dot2(k0, qe, s[0][h]);
+          s[1][h] = dot2(k1, qe, s[1][h]);
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < kGroup; ++h) asm volatile("" : "+v"(s[0][h]), "+v"(s[1][h]));
+    }
+    // Sum over the token's four lanes: rows c >> 1 == 0 keep heads 0-3, then
+    // rows with c & 1 == 0 keep the first two of those: lane (r, c) ends
+    // with heads 2c and 2c + 1.
+    float s4[2][4], sc[2][2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int h = 0; h < 4; ++h) s4[mb][h] = split_sum_xor32(s[mb][h], s[mb][h + 4]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) sc[mb][j] = split_sum_xor16(s4[mb][j], s4[mb][j + 2]);
+    }
+
+    // Online softmax in the log2 domain.
+    float a[2][2], mx[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      a[0][j] = (t0 + r < n) ? sc[0][j] * scale_log2 : kNegInf;
+      a[1][j] = (t0 + 16 + r < n) ? sc[1][j] * scale_log2 : kNegInf;
+      mx[j] = row_max16(fmaxf(a[0][j], a[1][j]));   // finite: every tile holds a valid token
+    }
+    float mx_all[kGroup];
+    share_rows(mx, mx_all);
+#pragma unroll
+    for (int h = 0; h < kGroup; ++h) {
+      const float m_new = fmaxf(m_all[h], mx_all[h]);
+      const float alpha = __builtin_amdgcn_exp2f(m_all[h] - m_new);
+      m_all[h] = m_new;
+      acc[h][0] *= alpha;
+      acc[h][1] *= alpha;
+    }
+    float p[2][2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float m_new = fmaxf(m_own[j], mx[j]);
+      const float alpha = __builtin_amdgcn_exp2f(m_own[j] - m_new);
+      m_own[j] = m_new;
+      p[0][j] = __builtin_amdgcn_exp2f(a[0][j] - m_new);
+      p[1][j] = __builtin_amdgcn_exp2f(a[1][j] - m_new);
+      l_own[j] = l_own[j] * alpha + (p[0][j] + p[1][j]);
+    }
+
+    // V rows and P to LDS.
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+        *reinterpret_cast<u32x4*>(lw + (16 * mb + r) * kRowU16 + 32 * x + 8 * c) = t.v[mb][x];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        lp[((4 * mb + (r >> 2)) * kGroup + 2 * c + j) * 4 + (r & 3)] = bf16_bits(p[mb][j]);
+    }
+    lds_wave_sync();
+  }
+
+  __device__ __forceinline__ void back(int r, int c, const uint16_t* lw) {
+    const uint16_t* lp = lw + kTileTok * kRowU16 + kQU16;
+    // P.V over the 8 token quads: lane (r, c) reads tokens 4qd .. 4qd + 3 of
+    // dims 16c + r and 64 + 16c + r (the transposing read: lane 4j + i of a
+    // row addresses token 4qd + j, dims 16c + 4i .. +4).
+    const uint16_t* vb = lw + (r >> 2) * kRowU16 + 4 * (r & 3) + 16 * c;
+#pragma unroll
+    for (int q2 = 0; q2 < kTileTok / 8; ++q2) {
+      // two quads per LDS round trip: their 4 V^T reads and 8 P reads leave
+      // before any is used
+      __builtin_amdgcn_sched_barrier(0);
+      u32x2 vt[2][2];
+      u32x4 pq[2][kGroup / 2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int qd = 2 * q2 + u;
+#pragma unroll
+        for (int hi = 0; hi < 2; ++hi)
+          vt[u][hi] = __builtin_bit_cast(
+              u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                         (__attribute__((address_space(3))) i16x4*)(vb + 4 * qd * kRowU16 + 64 * hi)));
+#pragma unroll
+        for (int hp = 0; hp < kGroup / 2; ++hp)
+          pq[u][hp] = *reinterpret_cast<const u32x4*>(lp + (qd * kGroup + 2 * hp) * 4);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        asm volatile("" : "+v"(vt[u][0]), "+v"(vt[u][1]));
+#pragma unroll
+        for (int hp = 0; hp < kGroup / 2; ++hp) asm volatile("" : "+v"(pq[u][hp]));
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const uint32_t v00 = vt[u][0][0], v01 = vt[u][0][1], v10 = vt[u][1][0], v11 = vt[u][1][1];
+#pragma unroll
+        for (int hp = 0; hp < kGroup / 2; ++hp) {
+          // heads 2hp, 2hp + 1: P pairs (4qd, 4qd + 1), (4qd + 2, 4qd + 3) each
+          const uint32_t p0 = pq[u][hp][0], p1 = pq[u][hp][1], p2 = pq[u][hp][2], p3 = pq[u][hp][3];
+          acc[2 * hp][0] = dot2(v01, p1, dot2(v00, p0, acc[2 * hp][0]));
+          acc[2 * hp][1] = dot2(v11, p1, dot2(v10, p0, acc[2 * hp][1]));
+          acc[2 * hp + 1][0] = dot2(v01, p3, dot2(v00, p2, acc[2 * hp + 1][0]));
+          acc[2 * hp + 1][1] = dot2(v11, p3, dot2(v10, p2, acc[2 * hp + 1][1]));
+        }
+      }
+      // The products are done here: without this the compiler sinks them to
+      // the accumulators' next use in the following tile, keeping every P
+      // read of this tile live across the next tile's loads.
+#pragma unroll
+      for (int h = 0; h < kGroup; ++h) asm volatile("" : "+v"(acc[h][0]), "+v"(acc[h][1]));
+    }
+  }
+
+  __device__ __forceinline__ void finish(int b, int g, int slot, int r, int c,
+                                         uint16_t* __restrict__ out, float* __restrict__ lse,
+                                         float* __restrict__ part_o, float* __restrict__ part_lse) {
+    float l_row[2], inv_own[2], inv_all[kGroup];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      l_row[j] = row_sum16(l_own[j]);
+      inv_own[j] = 1.0f / l_row[j];
+    }
+    share_rows(inv_own, inv_all);
+    const int64_t head0 = static_cast<int64_t>(slot < 0 ? b : slot) * kHq + g * kGroup;
+    const int d0 = 16 * c + r;
+    if (slot < 0) {
+#pragma unroll
+      for (int h = 0; h < kGroup; ++h) {
+        uint16_t* o = out + (head0 + h) * kHeadDim + d0;
+        o[0] = bf16_bits(acc[h][0] * inv_all[h]);
+        o[64] = bf16_bits(acc[h][1] * inv_all[h]);
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < kGroup; ++h) {
+        float* o = part_o + (head0 + h) * kHeadDim + d0;
+        o[0] = acc[h][0] * inv_all[h];
+        o[64] = acc[h][1] * inv_all[h];
+      }
+    }
+    if (r == 0) {
+      float* dst = slot < 0 ? lse : part_lse;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) dst[head0 + 2 * c + j] = m_own[j] + __log2f(l_row[j]);
+    }
+  }
+};
 
 // Pool row (page * page_size + slot) of token j of a segment.
 template <bool kTable>
@@ -203,7 +526,7 @@ struct TokenRows<true> {
 // Decodes the n > 0 tokens of a segment of sequence b, whose pool rows `ids`
 // gives, with all four waves of the workgroup and writes either the final
 // out/lse (slot < 0) or a partial.
-template <bool kTable>
+template <bool kTable, class Engine>
 __device__ __forceinline__ void process_segment(
     const TokenRows<kTable>& ids, int b, int n, int slot, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k_pool, const uint16_t* __restrict__ v_pool,
@@ -213,7 +536,6 @@ __device__ __forceinline__ void process_segment(
   const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // KV head of this wave
   const int r = lane & 15;
   const int c = lane >> 4;
-  const int head = g * kGroup + r;   // a real query head only for r < kGroup
   const int last = n - 1;
 
   // The ids of the first two tiles are fetched first: they depend only on
@@ -224,101 +546,113 @@ __device__ __forceinline__ void process_segment(
   int32_t a0 = ids.fetch(ja0), a1 = ids.fetch(ja1);
   int32_t n0 = ids.fetch(jn0), n1 = ids.fetch(jn1);
 
-  // Q as the B operand: lane (r, c) holds q[head r][32x + 8c, +8) for k-step x.
-  // The 8 padding columns (r >= kGroup) repeat heads r - kGroup: their scores
-  // and outputs are computed and never stored, and every lane loads, so the
-  // compiler can count the loads in flight (a masked load made it wait for q
-  // before the first K/V loads).
-  u32x4 qf[4];
-  {
-    const uint16_t* qh =
-        q + (static_cast<int64_t>(b) * kHq + g * kGroup + (r & (kGroup - 1))) * kHeadDim + 8 * c;
-#pragma unroll
-    for (int x = 0; x < 4; ++x) qf[x] = *reinterpret_cast<const u32x4*>(qh + 32 * x);
-  }
+  // q of the wave's query heads (every lane loads, so the compiler can count
+  // the loads in flight: a masked load made it wait for q before the first
+  // K/V loads).
+  Engine eng;
+  eng.begin(q, b, g, r, c);
+  uint16_t* lw = lds + g * Engine::kWaveLdsU16;   // each wave owns its LDS slice
 
-  Softmax st;
-#pragma unroll
-  for (int db = 0; db < 8; ++db) st.acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  st.m = kNegInf;
-  st.l = 0.f;
-  uint16_t* lw = lds + g * kWaveLdsU16;   // each wave owns its LDS slice
-
-  // Software pipeline over a ring of kPipeTiles register buffers: while the
-  // oldest tile is computed, the next kPipeTiles - 1 tiles are in flight.
-  // Page ids are fetched one tile ahead of the K/V loads they feed and issued
-  // before them, so waiting for ids never waits for younger K/V loads. The
-  // loop is unrolled over the ring so every buffer index is a constant, its
-  // body has no early exit, and the empty asm statements keep each load group
-  // where it is written. Loads past the segment re-read its last row; the
-  // last n_tiles % kPipeTiles tiles are computed after the loop from the
-  // buffers the final iterations loaded.
+  // Software pipeline over a ring of two register tiles, unrolled over the
+  // ring so every buffer index is a constant and the loop body has no early
+  // exit; the empty asm statements keep each load group where it is written.
+  // Page ids are fetched ahead of the K/V loads they feed and issued before
+  // the K/V loads of the tile before, so waiting for ids never waits for
+  // younger K/V loads. Loads past the segment re-read its last row (all lanes
+  // the same row: one cache line per lane group), and an odd last tile is
+  // computed after the loop from the buffer the final iterations loaded.
+  //
+  // Engine::kEarlyLoads picks where the next loads go out. false: at tile T,
+  // load tile T + 1 into the buffer of tile T - 1, then compute T (one tile in
+  // flight during the compute; fastest for the short MFMA compute). true:
+  // front(T) consumes tile T's registers, tile T + 2 is loaded into them, then
+  // back(T) runs while tiles T + 1 and T + 2 are in flight (for the longer
+  // vector-ALU compute).
   const int n_tiles = (n + kTileTok - 1) / kTileTok;
   const int n_rounds = n_tiles / kPipeTiles;
   static_assert(kPipeTiles == 2, "the prologue below fills a ring of two tiles");
   Tile ring[kPipeTiles];
-  // The first two tiles' ids (fetched above) are all in before any K/V load,
-  // so the loop starts with the second tile's rows known and no load pending
-  // but the first tile's.
-  asm volatile("" : "+v"(a0), "+v"(a1), "+v"(n0), "+v"(n1));
-  load_tile(ring[0], k_pool, v_pool, ids.row_of(a0, ja0), ids.row_of(a1, ja1), g, c);
-  int32_t next0 = ids.row_of(n0, jn0);
-  int32_t next1 = ids.row_of(n1, jn1);
   int t0 = 0;
-  for (int round = 0; round < n_rounds; ++round) {
+  if constexpr (Engine::kEarlyLoads) {
+    const int jc0 = min(2 * kTileTok + r, last), jc1 = min(2 * kTileTok + 16 + r, last);
+    int32_t c0 = ids.fetch(jc0), c1 = ids.fetch(jc1);
+    // The first two tiles' ids (fetched above) are all in before any K/V
+    // load; the third tile's, fetched after q, may still be in flight.
+    asm volatile("" : "+v"(a0), "+v"(a1), "+v"(n0), "+v"(n1));
+    load_tile(ring[0], k_pool, v_pool, ids.row_of(a0, ja0), ids.row_of(a1, ja1), g, c);
+    load_tile(ring[1], k_pool, v_pool, ids.row_of(n0, jn0), ids.row_of(n1, jn1), g, c);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" : "+v"(c0), "+v"(c1));
+    int32_t next0 = ids.row_of(c0, jc0);
+    int32_t next1 = ids.row_of(c1, jc1);
+    for (int round = 0; round < n_rounds; ++round) {
 #pragma unroll
-    for (int k = 0; k < kPipeTiles; ++k) {
-      // compute tile round * kPipeTiles + k (ring[k]); load the tile
-      // kPipeTiles - 1 later into the buffer computed last; fetch the ids of
-      // the tile after that.
-      asm volatile("" ::: "memory");
-      const int tf = t0 + kTileTok * (k + kPipeTiles);
-      const int j0 = min(tf + r, last);
-      const int j1 = min(tf + 16 + r, last);
-      int32_t f0 = ids.fetch(j0);
-      int32_t f1 = ids.fetch(j1);
-      load_tile(ring[(k + kPipeTiles - 1) % kPipeTiles], k_pool, v_pool, next0, next1, g, c);
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_sched_barrier(0);
-      compute_tile(ring[k], t0 + kTileTok * k, n, qf, scale_log2, r, c, lw, st);
-      __builtin_amdgcn_sched_barrier(0);
-      // The fetched ids stay opaque until the compute above has been issued,
-      // so nothing derived from them is scheduled next to their loads (which
-      // would make the wave wait for loads it has just issued).
-      asm volatile("" : "+v"(f0), "+v"(f1));
-      next0 = ids.row_of(f0, j0);
-      next1 = ids.row_of(f1, j1);
-    }
-    t0 += kTileTok * kPipeTiles;
-  }
-  const int rest = n_tiles - n_rounds * kPipeTiles;
-#pragma unroll
-  for (int k = 0; k < kPipeTiles - 1; ++k)
-    if (k < rest) compute_tile(ring[k], t0 + kTileTok * k, n, qf, scale_log2, r, c, lw, st);
-
-  const float l_tot = sum_xor32(sum_xor16(st.l));
-  const float inv = 1.0f / l_tot;
-  const float lse2 = st.m + __log2f(l_tot);
-  if (r < kGroup) {
-    if (slot < 0) {
-      uint16_t* o = out + (static_cast<int64_t>(b) * kHq + head) * kHeadDim + 4 * c;
-#pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const f32x4 v = st.acc[db] * inv;
-        const u32x2 w = {static_cast<uint32_t>(bf16_bits(v[0])) |
-                             (static_cast<uint32_t>(bf16_bits(v[1])) << 16),
-                         static_cast<uint32_t>(bf16_bits(v[2])) |
-                             (static_cast<uint32_t>(bf16_bits(v[3])) << 16)};
-        *reinterpret_cast<u32x2*>(o + 16 * db) = w;
+      for (int k = 0; k < kPipeTiles; ++k) {
+        // front of tile T = 2 round + k (ring[k]); fetch the ids of tile
+        // T + 3; load tile T + 2 into ring[k]; back of tile T.
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        eng.front(ring[k], t0 + kTileTok * k, n, scale_log2, r, c, lw);
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" ::: "memory");
+        const int tf = t0 + kTileTok * (k + 3);
+        const int j0 = min(tf + r, last);
+        const int j1 = min(tf + 16 + r, last);
+        int32_t f0 = ids.fetch(j0);
+        int32_t f1 = ids.fetch(j1);
+        load_tile(ring[k], k_pool, v_pool, next0, next1, g, c);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        eng.back(r, c, lw);
+        __builtin_amdgcn_sched_barrier(0);
+        // The fetched ids stay opaque until the compute above has been
+        // issued, so nothing derived from them is scheduled next to their
+        // loads (which would make the wave wait for loads it has just issued).
+        asm volatile("" : "+v"(f0), "+v"(f1));
+        next0 = ids.row_of(f0, j0);
+        next1 = ids.row_of(f1, j1);
       }
-      if (c == 0) lse[b * kHq + head] = lse2;
-    } else {
-      float* o = part_o + (static_cast<int64_t>(slot) * kHq + head) * kHeadDim + 4 * c;
+      t0 += kTileTok * kPipeTiles;
+    }
+  } else {
+    // The first two tiles' ids (fetched above) are all in before any K/V
+    // load, so the loop starts with the second tile's rows known and no load
+    // pending but the first tile's.
+    asm volatile("" : "+v"(a0), "+v"(a1), "+v"(n0), "+v"(n1));
+    load_tile(ring[0], k_pool, v_pool, ids.row_of(a0, ja0), ids.row_of(a1, ja1), g, c);
+    int32_t next0 = ids.row_of(n0, jn0);
+    int32_t next1 = ids.row_of(n1, jn1);
+    for (int round = 0; round < n_rounds; ++round) {
 #pragma unroll
-      for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(o + 16 * db) = st.acc[db] * inv;
-      if (c == 0) part_lse[static_cast<int64_t>(slot) * kHq + head] = lse2;
+      for (int k = 0; k < kPipeTiles; ++k) {
+        // compute tile round * kPipeTiles + k (ring[k]); load the tile after
+        // it into the buffer computed last; fetch the ids of the tile after
+        // that.
+        asm volatile("" ::: "memory");
+        const int tf = t0 + kTileTok * (k + kPipeTiles);
+        const int j0 = min(tf + r, last);
+        const int j1 = min(tf + 16 + r, last);
+        int32_t f0 = ids.fetch(j0);
+        int32_t f1 = ids.fetch(j1);
+        load_tile(ring[(k + kPipeTiles - 1) % kPipeTiles], k_pool, v_pool, next0, next1, g, c);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        eng.front(ring[k], t0 + kTileTok * k, n, scale_log2, r, c, lw);
+        eng.back(r, c, lw);
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" : "+v"(f0), "+v"(f1));
+        next0 = ids.row_of(f0, j0);
+        next1 = ids.row_of(f1, j1);
+      }
+      t0 += kTileTok * kPipeTiles;
     }
   }
+  if (n_tiles > n_rounds * kPipeTiles) {
+    eng.front(ring[0], t0, n, scale_log2, r, c, lw);
+    eng.back(r, c, lw);
+  }
+  eng.finish(b, g, slot, r, c, out, lse, part_o, part_lse);
 }
 
 // One workgroup per worker: it walks its segments in order. The first
@@ -327,14 +661,14 @@ __device__ __forceinline__ void process_segment(
 // tok_begin, n); n = 0 if the worker has no segment), so its id loads leave
 // one memory round trip earlier than the worker's record, which still
 // supplies b, the slot and the segment range.
-template <bool kTable>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_partial_kernel(
+template <bool kTable, class Engine>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Engine::kWavesPerEu))) void decode_partial_kernel(
     const int32_t* __restrict__ workers, const int32_t* __restrict__ segments,
     const FirstSegments firsts, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k_pool, const uint16_t* __restrict__ v_pool, KvAddressing addr,
     float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ part_o, float* __restrict__ part_lse) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[kHkv * kWaveLdsU16];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kHkv * Engine::kWaveLdsU16];
   const int w = blockIdx.x;
   const bool first_in_args = w < kFirstArgWorkers;
   // Read (clamped in range) before any branch, so the loads go out together
@@ -347,7 +681,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   if (first_in_args) {
     if (n > 0) {
       const TokenRows<kTable> ids(addr, kTable ? f0 : 0, f1, kTable ? 0 : f0);
-      process_segment<kTable>(ids, wrec[0], n, wrec[3], q, k_pool, v_pool, scale_log2, out, lse,
+      process_segment<kTable, Engine>(ids, wrec[0], n, wrec[3], q, k_pool, v_pool, scale_log2, out, lse,
                               part_o, part_lse, lds);
     }
   }
@@ -359,7 +693,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int n = seg[2] - lo;
     if (n > 0) {
       const TokenRows<kTable> ids(addr, seg[0], lo, seg[4]);
-      process_segment<kTable>(ids, seg[0], n, seg[3], q, k_pool, v_pool, scale_log2, out, lse,
+      process_segment<kTable, Engine>(ids, seg[0], n, seg[3], q, k_pool, v_pool, scale_log2, out, lse,
                               part_o, part_lse, lds);
     }
   }
@@ -562,17 +896,16 @@ hipError_t launch_decode_partial(const int32_t* workers, const int32_t* segments
                                  const uint16_t* q, const uint16_t* k_pool,
                                  const uint16_t* v_pool, const KvAddressing& addr,
                                  float sm_scale_log2, uint16_t* out, float* lse, float* part_o,
-                                 float* part_lse, hipStream_t stream) {
+                                 float* part_lse, DecodeEngine engine, hipStream_t stream) {
   if (n_workers <= 0) return hipSuccess;
-  if (addr.kv_indptr == nullptr) {
-    hipLaunchKernelGGL(decode_partial_kernel<true>, dim3(n_workers), dim3(kThreads), 0, stream,
-                       workers, segments, firsts, q, k_pool, v_pool, addr,
-                       sm_scale_log2, out, lse, part_o, part_lse);
-  } else {
-    hipLaunchKernelGGL(decode_partial_kernel<false>, dim3(n_workers), dim3(kThreads), 0, stream,
-                       workers, segments, firsts, q, k_pool, v_pool, addr,
-                       sm_scale_log2, out, lse, part_o, part_lse);
-  }
+  const bool table = addr.kv_indptr == nullptr;
+  auto kernel = engine == DecodeEngine::kDot2
+                    ? (table ? decode_partial_kernel<true, Dot2Engine>
+                             : decode_partial_kernel<false, Dot2Engine>)
+                    : (table ? decode_partial_kernel<true, MfmaEngine>
+                             : decode_partial_kernel<false, MfmaEngine>);
+  hipLaunchKernelGGL(kernel, dim3(n_workers), dim3(kThreads), 0, stream, workers, segments, firsts,
+                     q, k_pool, v_pool, addr, sm_scale_log2, out, lse, part_o, part_lse);
   return hipGetLastError();
 }
 

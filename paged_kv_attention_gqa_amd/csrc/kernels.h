@@ -37,6 +37,11 @@ struct FirstSegments {
   int32_t v[3 * kFirstArgWorkers];
 };
 
+// Which units do the decode kernel's two contractions (q.k scores and P.V):
+// the matrix cores (v_mfma_f32_16x16x32_bf16, the 8 query heads of a KV head
+// padded to 16 columns) or the vector ALU (v_dot2c_f32_bf16).
+enum class DecodeEngine : int32_t { kMfma = 0, kDot2 = 1 };
+
 // One workgroup per worker; worker w decodes the segments [s_begin, s_end)
 // named by its record workers[8w .. 8w+8) = (the first segment's five fields,
 // s_begin, s_end, 0); segment records are 8 int32:
@@ -46,7 +51,7 @@ hipError_t launch_decode_partial(const int32_t* workers, const int32_t* segments
                                  const uint16_t* q, const uint16_t* k_pool,
                                  const uint16_t* v_pool, const KvAddressing& addr,
                                  float sm_scale_log2, uint16_t* out, float* lse, float* part_o,
-                                 float* part_lse, hipStream_t stream);
+                                 float* part_lse, DecodeEngine engine, hipStream_t stream);
 
 // Merges the split sequences' partials: one workgroup per (merge record
 // (b, first_slot, n_segments, 0), group of query heads). max_pieces is the

@@ -54,6 +54,55 @@ __device__ __forceinline__ float sum_xor32(float x) {
   return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
 }
 
+// One step of a sum that leaves different lanes with different results: lanes
+// with bit 5 clear get a[i] + a[i | 32], lanes with it set b[i & ~32] + b[i]
+// (v_permlane32_swap_b32 exchanges the upper half of its first operand with
+// the lower half of its second). Eight values per lane reduce over the lane
+// pair to four this way, with one exchange per pair of values.
+__device__ __forceinline__ float split_sum_xor32(float a, float b) {
+  const lane_u32x2 r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, a),
+                                                        __builtin_bit_cast(unsigned, b),
+                                                        false, false);
+  const unsigned x = r[0], y = r[1];
+  return __builtin_bit_cast(float, x) + __builtin_bit_cast(float, y);
+}
+
+// The same over lanes i and i ^ 16: lanes with bit 4 clear get a[i] +
+// a[i | 16], lanes with it set b[i & ~16] + b[i].
+__device__ __forceinline__ float split_sum_xor16(float a, float b) {
+  const lane_u32x2 r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, a),
+                                                        __builtin_bit_cast(unsigned, b),
+                                                        false, false);
+  const unsigned x = r[0], y = r[1];
+  return __builtin_bit_cast(float, x) + __builtin_bit_cast(float, y);
+}
+
+// Lane i reads lane sel(i) of its own row of 16 through DPP (dpp_ctrl codes:
+// quad permutations 0x00-0xff, row_mirror 0x140, row_half_mirror 0x141).
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xf, 0xf, false));
+}
+
+// Max and sum over the 16 lanes of a row (lanes 16k .. 16k + 15), the result
+// in every lane of the row: exchanges with lane i ^ 1 and i ^ 2 (quad
+// permutations), then with the mirrored lane of the half row and of the row,
+// which after the quad steps holds the other quad's and the other half's value.
+__device__ __forceinline__ float row_max16(float x) {
+  x = fmaxf(x, dpp_f32<0xb1>(x));    // quad_perm [1, 0, 3, 2]
+  x = fmaxf(x, dpp_f32<0x4e>(x));    // quad_perm [2, 3, 0, 1]
+  x = fmaxf(x, dpp_f32<0x141>(x));   // row_half_mirror
+  return fmaxf(x, dpp_f32<0x140>(x));   // row_mirror
+}
+
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp_f32<0xb1>(x);
+  x += dpp_f32<0x4e>(x);
+  x += dpp_f32<0x141>(x);
+  return x + dpp_f32<0x140>(x);
+}
+
 }  // namespace pkv
 
 #endif  // PKV_LANES_H_

@@ -38,7 +38,7 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_symbols()
-    assert len(names) == 18
+    assert len(names) == 19
     for name in names:
         assert hasattr(lib, name), name
         assert name in pkv.SIGNATURES, name
@@ -48,6 +48,23 @@ def test_status_strings(lib):
     for code in range(6):
         assert pkv.pkv_status_string(code)
     assert pkv.pkv_status_string(99) == "unknown status"
+
+
+def test_set_engine_rejects_unknown_codes(lib):
+    """pkv_plan_set_engine takes PKV_ENGINE_MFMA (0) and PKV_ENGINE_DOT2 (1);
+    anything else, or a NULL plan, is PKV_ERR_INVALID_ARG (host only)."""
+    ind = np.array([0, 5, 9], dtype=np.int32)
+    plan = pkv.pkv_plan_create(ind, num_cus=8)
+    for code in (pkv.PKV_ENGINE_MFMA, pkv.PKV_ENGINE_DOT2):
+        assert lib.pkv_plan_set_engine(plan.handle, code) == pkv.PKV_OK
+    for code in (-1, 2, 99):
+        assert lib.pkv_plan_set_engine(plan.handle, code) == pkv.PKV_ERR_INVALID_ARG
+        assert "engine" in pkv.pkv_last_error()
+    assert lib.pkv_plan_set_engine(None, 0) == pkv.PKV_ERR_INVALID_ARG
+    pkv.pkv_plan_set_engine(plan, "dot2")
+    pkv.pkv_plan_set_engine(plan, "mfma")
+    with pytest.raises(KeyError):
+        pkv.pkv_plan_set_engine(plan, "fma")
 
 
 def _indptr(lengths):

@@ -17,8 +17,9 @@
 // * One workgroup per worker of the plan: a cost-balanced run of the batch's tokens,
 //   as a list of (sequence, token range) segments. Wave w handles KV head w
 //   and its 8 query heads and walks each segment in tiles of 32 tokens.
-// * Both contractions run on v_mfma_f32_16x16x32_bf16, the 8 query heads
-//   padded to 16 MFMA columns:
+// * Both contractions run on v_mfma_f32_16x16x32_bf16 (MfmaEngine, the
+//   default; Dot2Engine below runs them on the vector ALU instead), the 8
+//   query heads padded to 16 MFMA columns:
 //     S^T[tok, h] = K[tok, :] . Q[h, :]        A = K rows as loaded, B = Q^T
 //     O^T[d, h]  += V^T[d, tok] . P^T[tok, h]  A = V^T read back from LDS, B = P^T
 //   The S^T accumulator leaves lane (r, c) = (lane % 16, lane / 16) with head r
@@ -32,7 +33,8 @@
 // * V is written to LDS row-major (288-byte padded rows) and read back as the
 //   transposed A operand (8 tokens of one dim per lane) with the
 //   transposing LDS load ds_read_b64_tr_b16, two per 16-dim block.
-// * Loads are software-pipelined one tile ahead (page ids two tiles ahead);
+// * Loads are software-pipelined one tile ahead (page ids two tiles ahead;
+//   the vector-ALU engine issues them earlier, see process_segment);
 //   out-of-range tokens of the last tile re-read the item's last page, which
 //   keeps every load unconditional, and get score -inf, i.e. weight exactly 0.
 // * Scores are scaled by sm_scale*log2(e) in fp32 and exponentiated with

@@ -374,7 +374,7 @@ def main():
     ap.add_argument("--chunk", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--event-every", type=int, default=10,
-                    help="bracket the decode kernel with HIP events on every n-th timed step")
+                    help="time the decode kernel with HIP events on every n-th timed step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration runs)")
@@ -442,22 +442,32 @@ def main():
         merge()
     torch.cuda.synchronize()
 
-    # HIP events bracket the decode kernel on every `event_every`-th step of the
-    # timed loop (each event pair adds a few microseconds of queue work, so it
-    # is not put on every step); the kernel's mean duration comes from them.
+    # On every `event_every`-th step of the timed loop the decode launch itself
+    # records the kernel's start and end into a pair of HIP events
+    # (pkv_plan_set_timing_events, hipExtLaunchKernel), so their difference is
+    # the kernel's duration on the stream it runs on, without the queue time
+    # of separately recorded events; the kernel's mean duration comes from them.
     stream = torch.cuda.current_stream()
     every = max(1, args.event_every)
     sampled = list(range(0, args.steps, every))
     ev = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for i in sampled}
+    for a, b in ev.values():   # torch creates the HIP events at their first record
+        a.record(stream)
+        b.record(stream)
     torch.cuda.synchronize()
+    pkv.pkv_plan_set_timing_events(plan, *ev[0])   # checks the events once
+    pkv.pkv_plan_set_timing_events(plan)
+    # In the loop the binding is the bare C call (no Python-side checks).
+    bind, handle = pkv.lib().pkv_plan_set_timing_events, plan.handle
+    handles = {i: (a.cuda_event, b.cuda_event) for i, (a, b) in ev.items()}
     t0 = time.perf_counter()
     for i in range(args.steps):
-        e = ev.get(i)
-        if e is not None:
-            e[0].record(stream)
+        h = handles.get(i)
+        if h is not None:
+            bind(handle, h[0], h[1])
             runs[i % reps]()
-            e[1].record(stream)
+            bind(handle, None, None)
         else:
             runs[i % reps]()
         merge()

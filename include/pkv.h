@@ -133,6 +133,20 @@ enum { PKV_ENGINE_MFMA = 0, PKV_ENGINE_DOT2 = 1 };
 pkv_status pkv_plan_set_engine(pkv_plan* plan, int32_t engine);
 
 /*
+ * Timing hook, for benchmarks and profilers that time the decode kernel with
+ * events: while start_event and stop_event (hipEvent_t values the caller
+ * created, with timing enabled) are set, the decode kernel enqueued by
+ * pkv_run / pkv_block_table_run with this plan records its own start and end
+ * time in them (hipExtLaunchKernel), so hipEventElapsedTime gives the
+ * kernel's duration without the queue time of separately recorded events.
+ * Both NULL (the default) launches without events; exactly one NULL returns
+ * PKV_ERR_INVALID_ARG. The plan keeps the handles and does not own them: the
+ * caller keeps the events alive while they are set. Not for launches under
+ * stream capture. Host only.
+ */
+pkv_status pkv_plan_set_timing_events(pkv_plan* plan, void* start_event, void* stop_event);
+
+/*
  * Copy the plan's integer tables to host memory:
  * [n_workers, n_segments, n_merges, n_slots], then n_workers + 1 offsets of
  * each worker's first segment, then n_segments records

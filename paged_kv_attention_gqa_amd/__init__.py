@@ -21,6 +21,7 @@ __all__ = [
     "PkvError", "Plan", "decode", "gather_mla", "library_path",
     "pkv_workspace_size", "pkv_plan_create", "pkv_plan_destroy", "pkv_plan_export",
     "pkv_plan_workspace_size", "pkv_plan_upload", "pkv_plan_set_engine",
+    "pkv_plan_set_timing_events",
     "PKV_ENGINE_MFMA", "PKV_ENGINE_DOT2",
     "pkv_run", "pkv_merge", "pkv_gather_mla_workspace_size", "pkv_gather_mla",
     "prepare_run", "prepare_merge", "prepare_gather_mla", "prepare_append_kv",
@@ -57,6 +58,7 @@ SIGNATURES = {
     "pkv_plan_workspace_size": (_I32, [_P, _c.POINTER(_SZ)]),
     "pkv_plan_upload": (_I32, [_P, _P, _SZ, _P]),
     "pkv_plan_set_engine": (_I32, [_P, _I32]),
+    "pkv_plan_set_timing_events": (_I32, [_P, _P, _P]),
     "pkv_plan_export": (_I32, [_P, _I32P, _SZ, _c.POINTER(_SZ)]),
     "pkv_run": (_I32, [_P, _P, _I32, _I32, _I32, _P, _P, _I64, _I32, _I32, _I32, _P, _I64, _P,
                        _I64, _c.c_float, _P, _SZ, _P, _P, _P]),
@@ -509,6 +511,18 @@ def pkv_plan_set_engine(plan: Plan, engine) -> None:
     (the default) or ``"dot2"``, or the integer PKV_ENGINE_* code."""
     code = ENGINES[engine] if isinstance(engine, str) else int(engine)
     _check(lib().pkv_plan_set_engine(plan.handle, code), "pkv_plan_set_engine")
+
+
+def pkv_plan_set_timing_events(plan: Plan, start_event=None, stop_event=None) -> None:
+    """Let the plan's decode launches record their own start/stop time into two
+    torch.cuda.Event objects (already recorded once, so that they exist), or
+    stop doing so with no events."""
+    handles = []
+    for ev in (start_event, stop_event):
+        if ev is not None and not ev.cuda_event:
+            raise ValueError("record the event once before binding it (torch creates it lazily)")
+        handles.append(None if ev is None else ev.cuda_event)
+    _check(lib().pkv_plan_set_timing_events(plan.handle, *handles), "pkv_plan_set_timing_events")
 
 
 def pkv_plan_upload(plan: Plan, workspace, stream=None) -> None:

@@ -31,6 +31,7 @@ struct pkv_plan {
   pkv::FirstSegments firsts{};   // first segments' id positions, for the kernel arguments
   int32_t max_pieces = 0;        // most segments of one merge record
   pkv::DecodeEngine engine = pkv::DecodeEngine::kMfma;   // units of the decode contractions
+  hipEvent_t start_event = nullptr, stop_event = nullptr;  // timing hook (both or neither)
   size_t off_wptr, off_segs, off_merges, off_part_o, off_part_lse, ws_bytes;
   void* workspace;               // device buffer the tables were uploaded to (or NULL)
 };
@@ -325,8 +326,8 @@ pkv_status launch_run(const pkv_plan* plan, const void* q, const void* k_pool, c
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pool),
       static_cast<const uint16_t*>(v_pool), addr, sm_scale * log2e, static_cast<uint16_t*>(out),
       lse, reinterpret_cast<float*>(ws + plan->off_part_o),
-      reinterpret_cast<float*>(ws + plan->off_part_lse), plan->engine,
-      static_cast<hipStream_t>(stream));
+      reinterpret_cast<float*>(ws + plan->off_part_lse), plan->engine, plan->start_event,
+      plan->stop_event, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -461,6 +462,15 @@ pkv_status pkv_plan_set_engine(pkv_plan* plan, int32_t engine) {
     return fail(PKV_ERR_INVALID_ARG, "engine must be PKV_ENGINE_MFMA (0) or PKV_ENGINE_DOT2 (1), got %d",
                 engine);
   plan->engine = static_cast<pkv::DecodeEngine>(engine);
+  return ok();
+}
+
+pkv_status pkv_plan_set_timing_events(pkv_plan* plan, void* start_event, void* stop_event) {
+  if (plan == nullptr) return fail(PKV_ERR_INVALID_ARG, "plan is NULL");
+  if ((start_event == nullptr) != (stop_event == nullptr))
+    return fail(PKV_ERR_INVALID_ARG, "start_event and stop_event must both be set or both NULL");
+  plan->start_event = static_cast<hipEvent_t>(start_event);
+  plan->stop_event = static_cast<hipEvent_t>(stop_event);
   return ok();
 }
 

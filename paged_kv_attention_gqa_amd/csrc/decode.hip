@@ -41,6 +41,7 @@
 //   exp2; the running max is reduced across the 4 lane rows with the
 //   cross-lane swaps v_permlane16_swap / v_permlane32_swap (vector ALU, no
 //   LDS), the running sum is kept per lane and reduced once at the end.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
@@ -898,7 +899,8 @@ hipError_t launch_decode_partial(const int32_t* workers, const int32_t* segments
                                  const uint16_t* q, const uint16_t* k_pool,
                                  const uint16_t* v_pool, const KvAddressing& addr,
                                  float sm_scale_log2, uint16_t* out, float* lse, float* part_o,
-                                 float* part_lse, DecodeEngine engine, hipStream_t stream) {
+                                 float* part_lse, DecodeEngine engine, hipEvent_t start_event,
+                                 hipEvent_t stop_event, hipStream_t stream) {
   if (n_workers <= 0) return hipSuccess;
   const bool table = addr.kv_indptr == nullptr;
   auto kernel = engine == DecodeEngine::kDot2
@@ -906,8 +908,15 @@ hipError_t launch_decode_partial(const int32_t* workers, const int32_t* segments
                              : decode_partial_kernel<false, Dot2Engine>)
                     : (table ? decode_partial_kernel<true, MfmaEngine>
                              : decode_partial_kernel<false, MfmaEngine>);
-  hipLaunchKernelGGL(kernel, dim3(n_workers), dim3(kThreads), 0, stream, workers, segments, firsts,
-                     q, k_pool, v_pool, addr, sm_scale_log2, out, lse, part_o, part_lse);
+  if (start_event != nullptr) {
+    // The events take the kernel's own start and end times.
+    hipExtLaunchKernelGGL(kernel, dim3(n_workers), dim3(kThreads), 0, stream, start_event,
+                          stop_event, 0, workers, segments, firsts, q, k_pool, v_pool, addr,
+                          sm_scale_log2, out, lse, part_o, part_lse);
+  } else {
+    hipLaunchKernelGGL(kernel, dim3(n_workers), dim3(kThreads), 0, stream, workers, segments,
+                       firsts, q, k_pool, v_pool, addr, sm_scale_log2, out, lse, part_o, part_lse);
+  }
   return hipGetLastError();
 }
 

@@ -43,6 +43,8 @@ struct FirstSegments {
 enum class DecodeEngine : int32_t { kMfma = 0, kDot2 = 1 };
 
 // One workgroup per worker; worker w decodes the segments [s_begin, s_end)
+// (start_event / stop_event: NULL, or events that take the kernel's own start
+// and end times)
 // named by its record workers[8w .. 8w+8) = (the first segment's five fields,
 // s_begin, s_end, 0); segment records are 8 int32:
 // (b, tok_begin, tok_end, slot, kv_indptr[b], 0, 0, 0).
@@ -51,7 +53,8 @@ hipError_t launch_decode_partial(const int32_t* workers, const int32_t* segments
                                  const uint16_t* q, const uint16_t* k_pool,
                                  const uint16_t* v_pool, const KvAddressing& addr,
                                  float sm_scale_log2, uint16_t* out, float* lse, float* part_o,
-                                 float* part_lse, DecodeEngine engine, hipStream_t stream);
+                                 float* part_lse, DecodeEngine engine, hipEvent_t start_event,
+                                 hipEvent_t stop_event, hipStream_t stream);
 
 // Merges the split sequences' partials: one workgroup per (merge record
 // (b, first_slot, n_segments, 0), group of query heads). max_pieces is the

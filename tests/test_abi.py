@@ -38,7 +38,7 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_symbols()
-    assert len(names) == 19
+    assert len(names) == 20
     for name in names:
         assert hasattr(lib, name), name
         assert name in pkv.SIGNATURES, name
@@ -65,6 +65,18 @@ def test_set_engine_rejects_unknown_codes(lib):
     pkv.pkv_plan_set_engine(plan, "mfma")
     with pytest.raises(KeyError):
         pkv.pkv_plan_set_engine(plan, "fma")
+
+
+def test_set_timing_events_arguments(lib):
+    """Both events or neither; a NULL plan is rejected (host only)."""
+    ind = np.array([0, 5, 9], dtype=np.int32)
+    plan = pkv.pkv_plan_create(ind, num_cus=8)
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.pkv_plan_set_timing_events(plan.handle, fake, None) == pkv.PKV_ERR_INVALID_ARG
+    assert lib.pkv_plan_set_timing_events(plan.handle, None, fake) == pkv.PKV_ERR_INVALID_ARG
+    assert "both" in pkv.pkv_last_error()
+    assert lib.pkv_plan_set_timing_events(None, None, None) == pkv.PKV_ERR_INVALID_ARG
+    assert lib.pkv_plan_set_timing_events(plan.handle, None, None) == pkv.PKV_OK
 
 
 def _indptr(lengths):

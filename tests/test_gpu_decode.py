@@ -122,6 +122,42 @@ def test_split_matches_nosplit():
     assert np.max(np.abs(a[1] - b[1])) <= 1e-3
 
 
+def test_timing_events_leave_results_unchanged():
+    """A decode launched with timing events bound to its plan gives the same
+    bits as one without, the events hold a positive duration shorter than the
+    whole batch's wall time, and unbinding them restores plain launches."""
+    w = workload("gqa")
+    dev = upload_gqa(w)
+    plan = pkv.pkv_plan_create(w.kv_indptr)
+    ws = torch.empty(max(pkv.pkv_plan_workspace_size(plan), 16), dtype=torch.uint8, device="cuda")
+    pkv.pkv_plan_upload(plan, ws)
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with pytest.raises(ValueError):
+        pkv.pkv_plan_set_timing_events(plan, a, b)   # not created yet
+    a.record(stream)
+    b.record(stream)
+    results = []
+    for timed in (False, True, False):
+        out = torch.empty_like(dev["q"])
+        lse = torch.empty(dev["q"].shape[:2], dtype=torch.float32, device="cuda")
+        if timed:
+            pkv.pkv_plan_set_timing_events(plan, a, b)
+        pkv.pkv_run(plan, dev["q"], dev["k"], dev["v"], dev["indptr"], dev["indices"],
+                    w.sm_scale, ws, out, lse)
+        if timed:
+            pkv.pkv_plan_set_timing_events(plan)
+        pkv.pkv_merge(plan, ws, out, lse)
+        torch.cuda.synchronize()
+        results.append((bf16_to_np(out), lse.cpu().numpy()))
+        if timed:
+            ms = a.elapsed_time(b)
+            assert 0.0 < ms < 50.0, ms
+    for r in results[1:]:
+        assert np.array_equal(r[0], results[0][0]) and np.array_equal(r[1], results[0][1])
+    check(w, oracle("gqa"), (results[1][0], results[1][1].astype(np.float64)), "timed run")
+
+
 def test_rerun_bit_identical():
     w = workload("gqa")
     dev = upload_gqa(w)

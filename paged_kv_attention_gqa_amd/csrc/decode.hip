@@ -229,7 +229,7 @@ struct MfmaEngine {
     if (r < kGroup) {
       if (slot < 0) {
         uint16_t* o = out + (static_cast<int64_t>(b) * kHq + head) * kHeadDim + 4 * c;
-  #pragma unroll
+#pragma unroll
         for (int db = 0; db < 8; ++db) {
           const f32x4 v = st.acc[db] * inv;
           const u32x2 w = {static_cast<uint32_t>(bf16_bits(v[0])) |
@@ -241,7 +241,7 @@ struct MfmaEngine {
         if (c == 0) lse[b * kHq + head] = lse2;
       } else {
         float* o = part_o + (static_cast<int64_t>(slot) * kHq + head) * kHeadDim + 4 * c;
-  #pragma unroll
+#pragma unroll
         for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(o + 16 * db) = st.acc[db] * inv;
         if (c == 0) part_lse[static_cast<int64_t>(slot) * kHq + head] = lse2;
       }

@@ -271,14 +271,17 @@ def test_prepared_calls_match():
     check(w, oracle("edge"), (bf16_to_np(out), lse.cpu().numpy().astype(np.float64)), "prepared")
 
 
-def test_hip_graph_replay_matches_eager():
+@pytest.mark.parametrize("engine", ["mfma", "dot2"])
+def test_hip_graph_replay_matches_eager(engine):
     """run + merge captured once in a HIP graph and replayed several times, with
     eager work and synchronisations between replays: every replay equals the
-    eager result bit for bit (the calls enqueue kernels only)."""
+    eager result bit for bit (the calls enqueue kernels only), with either
+    contraction engine."""
     w = workload("edge")
     dev = upload_gqa(w)
     ws = torch.empty(pkv.pkv_workspace_size(w.kv_indptr), dtype=torch.uint8, device="cuda")
     plan = pkv.pkv_plan_create(w.kv_indptr, workspace=ws)
+    pkv.pkv_plan_set_engine(plan, engine)
     out = torch.empty_like(dev["q"])
     lse = torch.empty(dev["q"].shape[:2], dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()

@@ -56,8 +56,9 @@ def _place(pool_view, phys, rows_bits):
         (len(phys),) + tuple(pool_view.shape[1:]))
 
 
+@pytest.mark.parametrize("engine", ["mfma", "dot2"])
 @pytest.mark.parametrize("chunk", [0, 64])
-def test_csr_pages_across_2_31_elements(big_pools, chunk):
+def test_csr_pages_across_2_31_elements(big_pools, chunk, engine):
     k, v = big_pools
     w = make_gqa(710 + chunk, LENGTHS)
     n = w.k_pool.shape[0]
@@ -70,10 +71,10 @@ def test_csr_pages_across_2_31_elements(big_pools, chunk):
     indptr = to_dev(w.kv_indptr)
     out, lse = pkv.decode(q, k.view(ROWS, 1, HKV, D), v.view(ROWS, 1, HKV, D), indptr,
                           to_dev(indices), w.sm_scale, kv_indptr_host=w.kv_indptr,
-                          chunk_tokens=chunk)
+                          chunk_tokens=chunk, engine=engine)
     ref_out, ref_lse = pkv.decode(q, to_dev(w.k_pool), to_dev(w.v_pool), indptr,
                                   to_dev(w.kv_indices), w.sm_scale, kv_indptr_host=w.kv_indptr,
-                                  chunk_tokens=chunk)
+                                  chunk_tokens=chunk, engine=engine)
     torch.cuda.synchronize()
     want = ref.gqa_paged_decode(w.q, w.k_pool, w.v_pool, w.kv_indptr, w.kv_indices, w.sm_scale)
     assert_out_close(bf16_to_np(out), want[0], "big pool out")
@@ -82,8 +83,9 @@ def test_csr_pages_across_2_31_elements(big_pools, chunk):
     assert torch.equal(lse, ref_lse)
 
 
+@pytest.mark.parametrize("engine", ["mfma", "dot2"])
 @pytest.mark.parametrize("chunk", [0, 64])
-def test_block_table_pages_across_2_31_elements(big_pools, chunk):
+def test_block_table_pages_across_2_31_elements(big_pools, chunk, engine):
     ps = 16
     k, v = big_pools
     pages = ROWS // ps
@@ -102,10 +104,10 @@ def test_block_table_pages_across_2_31_elements(big_pools, chunk):
     assert table.max() >= boundary
     q = to_dev(w.q)
     out, lse = pkv.decode_block_table(q, kp, vp, to_dev(table), w.seq_lens, w.sm_scale,
-                                      chunk_tokens=chunk)
+                                      chunk_tokens=chunk, engine=engine)
     ref_out, ref_lse = pkv.decode_block_table(q, to_dev(w.k_pool), to_dev(w.v_pool),
                                               to_dev(w.block_table), w.seq_lens, w.sm_scale,
-                                              chunk_tokens=chunk)
+                                              chunk_tokens=chunk, engine=engine)
     torch.cuda.synchronize()
     want = ref.gqa_block_table_decode(w.q, w.k_pool, w.v_pool, w.block_table, w.seq_lens,
                                       w.sm_scale)

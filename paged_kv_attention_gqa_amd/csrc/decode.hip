@@ -33,8 +33,11 @@
 // * V is written to LDS row-major (288-byte padded rows) and read back as the
 //   transposed A operand (8 tokens of one dim per lane) with the
 //   transposing LDS load ds_read_b64_tr_b16, two per 16-dim block.
-// * Loads are software-pipelined one tile ahead (page ids two tiles ahead;
-//   the vector-ALU engine issues them earlier, see process_segment);
+// * Loads are software-pipelined one tile ahead, page ids two tiles ahead
+//   (for a CSR page list staged through a 128-byte LDS slot per wave: one
+//   coalesced read of a tile's 32 ids, then two LDS reads per lane; the
+//   vector-ALU engine issues loads earlier and keeps ids in registers, see
+//   process_segment);
 //   out-of-range tokens of the last tile re-read the item's last page, which
 //   keeps every load unconditional, and get score -inf, i.e. weight exactly 0.
 // * Scores are scaled by sm_scale*log2(e) in fp32 and exponentiated with
@@ -189,7 +192,8 @@ __device__ __forceinline__ void compute_back(const bf16x8& pb, int r, int c, con
 // MfmaEngine: both contractions on v_mfma_f32_16x16x32_bf16 (compute_front,
 // compute_back).
 struct MfmaEngine {
-  static constexpr int kWaveLdsU16 = kTileTok * kRowU16;   // the V tile
+  static constexpr int kIdSlotU16 = kTileTok * kRowU16;       // after the V tile: 32 page ids
+  static constexpr int kWaveLdsU16 = kIdSlotU16 + 2 * kTileTok;
   static constexpr int kWavesPerEu = 2;
   static constexpr bool kEarlyLoads = false;
   u32x4 qf[4];
@@ -271,6 +275,7 @@ struct Dot2Engine {
   static constexpr int kQU16 = kGroup * kHeadDim;   // the wave's q block, row-major by head
   static constexpr int kPU16 = kTileTok * kGroup;   // P of one tile
   static constexpr int kWaveLdsU16 = kTileTok * kRowU16 + kQU16 + kPU16;
+  static constexpr int kIdSlotU16 = -1;   // the early-load pipeline keeps page ids in registers
   static constexpr int kWavesPerEu = 2;
   static constexpr bool kEarlyLoads = true;
   u32x4 qa, qb;          // bytes [32 lane, +32) of the q block, until they go to LDS
@@ -636,17 +641,39 @@ __device__ __forceinline__ void process_segment(
         const int tf = t0 + kTileTok * (k + kPipeTiles);
         const int j0 = min(tf + r, last);
         const int j1 = min(tf + 16 + r, last);
-        int32_t f0 = ids.fetch(j0);
-        int32_t f1 = ids.fetch(j1);
+        int32_t f0, f1 = 0;
+        if constexpr (kTable) {
+          f0 = ids.fetch(j0);
+          f1 = ids.fetch(j1);
+        } else {
+          // The page list is staged through LDS: lanes 16c + r (c < 2) load
+          // the tile's 32 ids in one coalesced 128-byte read (lanes c >= 2
+          // repeat it), and after the compute below they go to the wave's
+          // id slot, from which every lane reads the two it needs.
+          f0 = ids.fetch(min(tf + ((16 * c + r) & 31), last));
+        }
         load_tile(ring[(k + kPipeTiles - 1) % kPipeTiles], k_pool, v_pool, next0, next1, g, c);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
         eng.front(ring[k], t0 + kTileTok * k, n, scale_log2, r, c, lw);
         eng.back(r, c, lw);
         __builtin_amdgcn_sched_barrier(0);
-        asm volatile("" : "+v"(f0), "+v"(f1));
-        next0 = ids.row_of(f0, j0);
-        next1 = ids.row_of(f1, j1);
+        // The fetched ids stay opaque until the compute above has been
+        // issued, so nothing derived from them is scheduled next to their
+        // loads (which would make the wave wait for loads it has just issued).
+        if constexpr (kTable) {
+          asm volatile("" : "+v"(f0), "+v"(f1));
+          next0 = ids.row_of(f0, j0);
+          next1 = ids.row_of(f1, j1);
+        } else {
+          asm volatile("" : "+v"(f0));
+          int32_t* slot_ids = reinterpret_cast<int32_t*>(lw + Engine::kIdSlotU16);
+          lds_wave_sync();
+          if (c < 2) slot_ids[16 * c + r] = f0;
+          lds_wave_sync();
+          next0 = slot_ids[r];
+          next1 = slot_ids[16 + r];
+        }
       }
       t0 += kTileTok * kPipeTiles;
     }

@@ -96,7 +96,7 @@ def test_ragged_small(lengths, chunk):
     check(want, run_csr(w, chunk_tokens=chunk), f"dot2 ragged {lengths} chunk={chunk}")
 
 
-@pytest.mark.parametrize("ps", [16, 64])
+@pytest.mark.parametrize("ps", [1, 16, 64, 1024])
 def test_block_table_partial_pages(ps):
     lengths = [1, ps - 1, ps, ps + 1, 5 * ps + 3, 0]
     w = make_block_table(610 + ps, lengths, ps)

@@ -29,8 +29,9 @@ def random_lengths(rng, batch, max_len):
     return [int(x) for x in lengths]
 
 
+@pytest.mark.parametrize("engine", ["mfma", "dot2"])
 @pytest.mark.parametrize("seed", range(12))
-def test_random_csr_decode(seed):
+def test_random_csr_decode(seed, engine):
     rng = np.random.default_rng(1000 + seed)
     batch = int(rng.integers(1, 40))
     lengths = random_lengths(rng, batch, int(rng.choice([40, 300, 3000])))
@@ -41,15 +42,17 @@ def test_random_csr_decode(seed):
     chunk = int(rng.choice([0, 0, 32, 64, 100, 512]))
     dev = upload_gqa(w)
     out, lse = pkv.decode(dev["q"], dev["k"], dev["v"], dev["indptr"], dev["indices"], w.sm_scale,
-                          kv_indptr_host=w.kv_indptr, allow_split=split, chunk_tokens=chunk)
+                          kv_indptr_host=w.kv_indptr, allow_split=split, chunk_tokens=chunk,
+                          engine=engine)
     torch.cuda.synchronize()
     want = ref.gqa_paged_decode(w.q, w.k_pool, w.v_pool, w.kv_indptr, w.kv_indices, w.sm_scale)
     check(want, (bf16_to_np(out), lse.cpu().numpy().astype(np.float64)),
-          f"csr seed={seed} B={batch} split={split} chunk={chunk}")
+          f"csr {engine} seed={seed} B={batch} split={split} chunk={chunk}")
 
 
+@pytest.mark.parametrize("engine", ["mfma", "dot2"])
 @pytest.mark.parametrize("seed", range(10))
-def test_random_block_table_decode(seed):
+def test_random_block_table_decode(seed, engine):
     rng = np.random.default_rng(3000 + seed)
     batch = int(rng.integers(1, 30))
     ps = int(rng.choice([2, 8, 16, 64, 256]))
@@ -60,12 +63,12 @@ def test_random_block_table_decode(seed):
     chunk = int(rng.choice([0, 0, 64, 160]))
     out, lse = pkv.decode_block_table(to_dev(w.q), to_dev(w.k_pool), to_dev(w.v_pool),
                                       to_dev(w.block_table), w.seq_lens, w.sm_scale,
-                                      chunk_tokens=chunk)
+                                      chunk_tokens=chunk, engine=engine)
     torch.cuda.synchronize()
     want = ref.gqa_block_table_decode(w.q, w.k_pool, w.v_pool, w.block_table, w.seq_lens,
                                       w.sm_scale)
     check(want, (bf16_to_np(out), lse.cpu().numpy().astype(np.float64)),
-          f"table seed={seed} B={batch} ps={ps} chunk={chunk}")
+          f"table {engine} seed={seed} B={batch} ps={ps} chunk={chunk}")
 
 
 @pytest.mark.parametrize("seed", range(10))

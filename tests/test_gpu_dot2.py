@@ -164,3 +164,35 @@ def test_engine_switch_on_one_plan():
         pkv.pkv_merge(plan, ws, out, lse)
         torch.cuda.synchronize()
         check(want, (bf16_to_np(out), lse.cpu().numpy().astype(np.float64)), f"switch {engine}")
+
+
+@pytest.mark.parametrize("chunk", [0, 64])
+def test_exact_means_both_engines(chunk):
+    """Inputs whose result is exact in every accumulation order: K = 0 (every
+    score 0, so p = 1 and l counts the tokens), V = v0 +- 1/4 alternating over
+    the tokens with v0 on a grid of 1/8 in [-4, 4] (every sum exact in fp32),
+    and lengths and cuts that are multiples of 64 tokens (every piece holds as
+    many + as - rows). The output is then v0 exactly, for both engines, split
+    or not, through the merge's power-of-two weights."""
+    lengths = [64, 128, 256, 512, 1024]
+    w = make_gqa(630, lengths, pool_pages=sum(lengths) + 5)
+    rng = np.random.default_rng(631)
+    v0 = rng.integers(-32, 33, size=(len(lengths), 4, 128)).astype(np.float32) / 8.0
+    k = np.zeros(w.k_pool.shape, dtype=np.float32)
+    v = np.zeros(w.v_pool.shape, dtype=np.float32)
+    for b, n in enumerate(lengths):
+        for j in range(n):
+            page = w.kv_indices[w.kv_indptr[b] + j]
+            v[page, 0] = v0[b] + (0.25 if j % 2 == 0 else -0.25)
+    from inputs.configs import bf16_bits_from_f32
+    w.k_pool = bf16_bits_from_f32(k)
+    w.v_pool = bf16_bits_from_f32(v)
+    want = np.repeat(v0, 8, axis=1)   # query head h reads KV head h // 8
+    dev = upload_gqa(w)
+    outs = {}
+    for engine in ("mfma", "dot2"):
+        out, lse = run_csr(w, dev, engine=engine, chunk_tokens=chunk)
+        assert np.array_equal(out, want), engine
+        assert np.max(np.abs(lse - np.log2(np.array(lengths))[:, None])) <= 1e-6, engine
+        outs[engine] = (out, lse)
+    assert np.array_equal(outs["mfma"][1], outs["dot2"][1])
